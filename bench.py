@@ -1,0 +1,213 @@
+"""Benchmark: Gated DeltaNet layer prefill on one MI355X, through the C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload: one GDN layer with 16 key heads and 32 value heads of width 128, bf16 activations,
+fp32 state, width-4 causal conv with state, commit grid 512, sub-chunks of 64 rows; one step
+commits T = 8192 rows (conv, L2 norm, gates, WY/UT factors, the state chain, outputs and the
+new conv window).  Inputs are seeded synthetic tensors resident in HBM before timing starts;
+three input sets rotate so that consecutive steps do not re-read the previous step's inputs
+from the 256 MB Infinity Cache.
+
+Prints one JSON line (rank 0) with the whole-job tokens/s, a roofline object for the layer
+call measured with HIP events on the launch stream, and the float64 CPU oracle timed on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2516.6  # dense fp16 / bf16 MFMA
+T_ROWS = 8192
+SHAPE = dict(n_k_heads=16, n_v_heads=32, d=128)
+
+
+def algorithmic_bytes(T, Hk, Hv, d, act_bytes=2, out_bytes=2):
+    """HBM bytes the method must move per call: x (q|k|v) in, g and beta in, o out, the fp32
+    state in and out, the conv window in and out, the conv weights in."""
+    C = 2 * Hk * d + Hv * d
+    per_token = C * act_bytes + 2 * Hv * 4 + Hv * d * out_bytes
+    per_call = 2 * Hv * d * d * 4 + 2 * 3 * C * act_bytes + C * 4 * act_bytes
+    return per_token, per_token * T + per_call
+
+
+def algorithmic_flops(T, Hk, Hv, d, C=64):
+    """Flops of the chunked method per call: K K^T and Q K^T per key head (lower triangle),
+    and per value head the products with the state, the triangular T R and M D, and the
+    state update (dense attention is not counted)."""
+    mac_k = C * d                                        # per token per key head
+    mac_v = 3 * d * d + ((C - 1) / 2 + (C + 1) / 2) * d + C * C / 6
+    return 2.0 * T * (Hk * mac_k + Hv * mac_v)
+
+
+def cpu_baseline(seconds_target=15.0):
+    """The float64 oracle on a bounded sample: all 32 value heads of the same layer over the
+    first rows of the workload, threads over heads."""
+    import numpy as np
+    from hybrid_linear_attention_prefill_amd import synth
+    from oracle import c_oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    shape = synth.LAYER_16x32x128
+    kw = dict(n_k_heads=16, n_v_heads=32, d_k=128, d_v=128, scale=128 ** -0.5, l2_eps=1e-6)
+    rows = 256
+    while True:
+        inp = synth.layer_inputs(shape, rows, seed=0)
+        x, w = synth.f64(inp["x"]), synth.f64(inp["conv_w"])
+        g, beta = synth.f64(inp["g"]), synth.f64(inp["beta"])
+        t0 = time.perf_counter()
+        c_oracle.gdn_layer(x, w, np.zeros((3, shape.channels)), g, beta,
+                           np.zeros((32, 128, 128)), threads=threads, **kw)
+        dt = time.perf_counter() - t0
+        if dt < seconds_target / 3 and rows < T_ROWS:
+            rows = min(T_ROWS, rows * 2)
+            continue
+        return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                "sample": "float64 per-token oracle (conv, L2 norm, gated delta rule), all 32 "
+                          "value heads of the 16/32/128 layer over the first %d of the 8192 rows "
+                          "(%.1f s wall)" % (rows, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the layer's heads would shard across GPUs with no "
+              "exchange step, but that path is not built; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from hybrid_linear_attention_prefill_amd import binding as b
+    from hybrid_linear_attention_prefill_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    Hk, Hv, d = SHAPE["n_k_heads"], SHAPE["n_v_heads"], SHAPE["d"]
+    desc = b.make_desc(Hk, Hv, d, d, conv_width=4, grid=512)
+    shape = synth.LAYER_16x32x128
+
+    n_sets = 3
+    sets = []
+    for i in range(n_sets):
+        inp = synth.layer_inputs(shape, T_ROWS, seed=i)
+        sets.append({k: v.to(dev) for k, v in inp.items()})
+    o = torch.empty((T_ROWS, Hv, d), dtype=torch.bfloat16, device=dev)
+    ws = b.workspace(desc, T_ROWS, 1)
+    state = b.State(desc)
+    b.gdn_state_init(desc, state)
+
+    def step(i):
+        s = sets[i % n_sets]
+        n = b.gdn_prefill_chunked(desc, s["x"], s["conv_w"], s["g"], s["beta"], state, state, o,
+                                  T_ROWS, b.GDN_COMMIT, ws)
+        assert n == T_ROWS
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # per-kernel durations of the same call, events recorded by the library on the stream
+    per_kernel = {"prep_kernel": 0.0, "chain_kernel": 0.0, "window_kernel": 0.0}
+    reps = max(10, args.steps // 2)
+    for i in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        s = sets[i % n_sets]
+        b.gdn_prefill_chunked_events(desc, s["x"], s["conv_w"], s["g"], s["beta"], state, state, o,
+                                     T_ROWS, b.GDN_COMMIT, ws, events=evs)
+        torch.cuda.synchronize()
+        for k, name in enumerate(per_kernel):
+            per_kernel[name] += evs[2 * k].elapsed_time(evs[2 * k + 1]) / reps
+
+    # state copies (capture + restore of the 2 MiB state and window) and a fork of a
+    # 330-row pending tail plus a 40-row question above the committed rows
+    snap = b.State(desc)
+    fork_out = b.State(desc)
+    fo = torch.empty((370, Hv, d), dtype=torch.bfloat16, device=dev)
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps2 = 20
+    e2.record(stream)
+    for _ in range(reps2):
+        b.gdn_state_capture(desc, state, snap)
+        b.gdn_state_restore(desc, state, snap)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = e2.elapsed_time(e3) / reps2
+    copy_bytes = 2 * 2 * (b.gdn_state_S_bytes(desc) + b.gdn_state_conv_bytes(desc))
+    e2.record(stream)
+    for _ in range(reps2):
+        s = sets[0]
+        b.gdn_prefill_chunked(desc, s["x"][:370], s["conv_w"], s["g"][:370], s["beta"][:370],
+                              state, fork_out, fo, 370, b.GDN_FORK, ws)
+    e3.record(stream)
+    torch.cuda.synchronize()
+    fork_ms = e2.elapsed_time(e3) / reps2
+
+    per_token, bytes_call = algorithmic_bytes(T_ROWS, Hk, Hv, d)
+    flops_call = algorithmic_flops(T_ROWS, Hk, Hv, d)
+    achieved = bytes_call / (ev_ms * 1e-3) / 1e9
+    tokens_per_s = T_ROWS * args.steps / wall
+    out = {
+        "metric": "Gated-DeltaNet prefill tokens/sec per layer (1 MI355X); % of MFMA/HBM roofline",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 io, fp16 MFMA operands, fp32 accumulate and state",
+        "data": "synthetic",
+        "config": {"workload": "gdn_layer_commit_prefill", "T": T_ROWS, "n_k_heads": Hk,
+                   "n_v_heads": Hv, "d_k": d, "d_v": d, "conv_width": 4, "grid": 512,
+                   "sub_chunk": 64, "act_dtype": "bf16", "out_dtype": "bf16"},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "layer call: prep_kernel + chain_kernel + window_kernel",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_call": bytes_call,
+            "algorithmic_bytes_per_token": per_token,
+            "call_ms_events": round(ev_ms, 5),
+            "per_kernel_ms_events": {k: round(v, 5) for k, v in per_kernel.items()},
+            "mfma_tflops_algorithmic": round(flops_call / (ev_ms * 1e-3) / 1e12, 2),
+            "mfma_frac_algorithmic": round(flops_call / (ev_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+        },
+        "extras": {
+            "state_capture_restore_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+            "fork_370_rows_ms": round(fork_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,478 @@
+// gdn_host.cpp -- host half of libgdn_prefill.so: argument validation, the commit-grid
+// arithmetic, state copies and the launch sequence.  Every check runs before the first HIP
+// call, so a refused call enqueues nothing and changes no state (the pages refuse invalid
+// requests before any device work: PR "qwen3_5: run prompts that share prefixes once per
+// prefix", sections "Test Plan" and "Test Result").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int64_t n_channels(const gdn_desc &d)
+{
+    return 2 * (int64_t)d.n_k_heads * d.d_k + (int64_t)d.n_v_heads * d.d_v;
+}
+static size_t act_size(const gdn_desc &d) { return d.act_dtype == GDN_BF16 ? 2 : 4; }
+static size_t out_size(const gdn_desc &d) { return d.out_dtype == GDN_BF16 ? 2 : 4; }
+
+size_t workspace_bytes(const gdn_desc &d, int64_t n_sub)
+{
+    const size_t qk = align256((size_t)n_sub * d.n_k_heads * kC * d.d_k * 2);
+    const size_t tm = align256((size_t)n_sub * d.n_v_heads * kC * kC * 2);
+    const size_t gc = align256((size_t)n_sub * d.n_v_heads * kC * 4);
+    return 2 * qk + 2 * tm + gc;
+}
+
+Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base)
+{
+    const size_t qk = align256((size_t)n_sub * d.n_k_heads * kC * d.d_k * 2);
+    const size_t tm = align256((size_t)n_sub * d.n_v_heads * kC * kC * 2);
+    char *p = (char *)base;
+    Workspace w;
+    w.Qh = (_Float16 *)p;
+    w.Kh = (_Float16 *)(p + qk);
+    w.Tm = (_Float16 *)(p + 2 * qk);
+    w.Mm = (_Float16 *)(p + 2 * qk + tm);
+    w.Gc = (float *)(p + 2 * qk + 2 * tm);
+    return w;
+}
+
+static bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+// Memory of a state (S and window) as two ranges.
+struct Ranges {
+    const void *p[2];
+    size_t n[2];
+};
+static Ranges ranges_of(const gdn_desc &d, const gdn_state *s)
+{
+    Ranges r;
+    r.p[0] = s->S;
+    r.n[0] = gdn_state_S_bytes(&d);
+    r.p[1] = s->conv;
+    r.n[1] = gdn_state_conv_bytes(&d);
+    return r;
+}
+static bool states_overlap(const gdn_desc &d, const gdn_state *a, const gdn_state *b)
+{
+    const Ranges ra = ranges_of(d, a), rb = ranges_of(d, b);
+    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j)
+            if (overlap(ra.p[i], ra.n[i], rb.p[j], rb.n[j])) return true;
+    return false;
+}
+static bool states_same(const gdn_state *a, const gdn_state *b)
+{
+    return a == b || (a->S == b->S && a->conv == b->conv);
+}
+
+static gdn_status check_state(const gdn_desc &d, const gdn_state *s)
+{
+    if (!s || !s->S) return GDN_EINVAL;
+    if (d.conv_width > 0 && !s->conv) return GDN_EINVAL;
+    if (s->pos < 0) return GDN_EINVAL;
+    if (s->tag != gdn_desc_tag(&d)) return GDN_EMISMATCH;
+    return GDN_OK;
+}
+
+static gdn_status copy_state(const gdn_desc &d, const gdn_state *src, gdn_state *dst, void *stream)
+{
+    if (launch_copy(dst->S, src->S, gdn_state_S_bytes(&d), stream) != 0) return GDN_EDEVICE;
+    if (d.conv_width > 0 &&
+        launch_copy(dst->conv, src->conv, gdn_state_conv_bytes(&d), stream) != 0)
+        return GDN_EDEVICE;
+    return GDN_OK;
+}
+
+// Runs the kernels over `segs` (already validated), cutting them into launches of at most
+// kMaxSegPerLaunch sequences.  Each launch reuses the workspace from its start; launches are
+// ordered on the stream.
+static gdn_status run_segments(const gdn_desc &d, const std::vector<Seg> &segs, const void *x,
+                               const void *conv_w, const float *g, const float *beta, void *o,
+                               void *ws, void *stream, void *const *events = nullptr,
+                               int n_events = 0)
+{
+    for (size_t b = 0; b < segs.size(); b += kMaxSegPerLaunch) {
+        SegArgs sa;
+        std::memset(&sa, 0, sizeof(sa));
+        const size_t e = std::min(segs.size(), b + (size_t)kMaxSegPerLaunch);
+        int32_t sub = 0;
+        for (size_t i = b; i < e; ++i) {
+            Seg s = segs[i];
+            s.sub0 = sub;
+            sub += (s.n + kC - 1) / kC;
+            sa.seg[sa.n_seg++] = s;
+        }
+        sa.n_sub = sub;
+        if (sub == 0) continue;
+        const Workspace w = carve_workspace(d, sub, ws);
+        if (launch_prefill(d, sa, x, conv_w, g, beta, o, w, stream, b == 0 ? events : nullptr,
+                           n_events) != 0)
+            return GDN_EDEVICE;
+    }
+    return GDN_OK;
+}
+
+// Largest per-launch sub-chunk count of `segs`.
+static int64_t max_launch_subs(const std::vector<Seg> &segs)
+{
+    int64_t best = 0;
+    for (size_t b = 0; b < segs.size(); b += kMaxSegPerLaunch) {
+        int64_t sub = 0;
+        for (size_t i = b; i < std::min(segs.size(), b + (size_t)kMaxSegPerLaunch); ++i)
+            sub += (segs[i].n + kC - 1) / kC;
+        best = std::max(best, sub);
+    }
+    return best;
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+gdn_status gdn_desc_check(const gdn_desc *d)
+{
+    if (!d) return GDN_EINVAL;
+    if (d->n_k_heads <= 0 || d->n_v_heads <= 0 || d->d_k <= 0 || d->d_v <= 0) return GDN_EINVAL;
+    if (d->act_dtype != GDN_BF16 && d->act_dtype != GDN_F32) return GDN_EINVAL;
+    if (d->out_dtype != GDN_BF16 && d->out_dtype != GDN_F32) return GDN_EINVAL;
+    if (d->conv_silu != 0 && d->conv_silu != 1) return GDN_EINVAL;
+    if (!(d->l2_eps >= 0.f) || !(d->scale == d->scale)) return GDN_EINVAL;
+    if (d->n_v_heads % d->n_k_heads != 0) return GDN_ESHAPE;
+    if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return GDN_ESHAPE;
+    if (d->conv_width != 0 && d->conv_width != 4) return GDN_ESHAPE;
+    if (d->sub_chunk != GDN_SUB_CHUNK) return GDN_ESHAPE;
+    if (d->grid <= 0 || d->grid % GDN_SUB_CHUNK != 0) return GDN_ESHAPE;
+    if (n_channels(*d) > (int64_t)1 << 24) return GDN_ESHAPE;
+    return GDN_OK;
+}
+
+uint64_t gdn_desc_tag(const gdn_desc *d)
+{
+    if (!d) return 0;
+    const int32_t f[8] = {d->n_k_heads, d->n_v_heads, d->d_k,  d->d_v,
+                          d->conv_width, d->sub_chunk, d->grid, d->act_dtype};
+    uint64_t h = 1469598103934665603ull;  // FNV-1a offset basis
+    const unsigned char *p = (const unsigned char *)f;
+    for (size_t i = 0; i < sizeof(f); ++i) {
+        h ^= p[i];
+        h *= 1099511628211ull;  // FNV prime
+    }
+    return h;
+}
+
+size_t gdn_state_S_bytes(const gdn_desc *d)
+{
+    if (gdn_desc_check(d) != GDN_OK) return 0;
+    return (size_t)d->n_v_heads * d->d_k * d->d_v * sizeof(float);
+}
+
+size_t gdn_state_conv_bytes(const gdn_desc *d)
+{
+    if (gdn_desc_check(d) != GDN_OK || d->conv_width == 0) return 0;
+    return (size_t)(d->conv_width - 1) * n_channels(*d) * act_size(*d);
+}
+
+size_t gdn_workspace_bytes(const gdn_desc *d, int64_t max_rows, int32_t max_segments)
+{
+    if (gdn_desc_check(d) != GDN_OK || max_rows < 0 || max_segments < 0) return 0;
+    return workspace_bytes(*d, max_rows / kC + max_segments);
+}
+
+gdn_status gdn_state_init(const gdn_desc *d, gdn_state *s, void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (!s || !s->S || (d->conv_width > 0 && !s->conv)) return GDN_EINVAL;
+    if (launch_zero(s->S, gdn_state_S_bytes(d), stream) != 0) return GDN_EDEVICE;
+    if (d->conv_width > 0 && launch_zero(s->conv, gdn_state_conv_bytes(d), stream) != 0)
+        return GDN_EDEVICE;
+    s->pos = 0;
+    s->tag = gdn_desc_tag(d);
+    return GDN_OK;
+}
+
+gdn_status gdn_state_capture(const gdn_desc *d, const gdn_state *live, gdn_state *snap,
+                             void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if ((st = check_state(*d, live))) return st;
+    if (!snap || !snap->S || (d->conv_width > 0 && !snap->conv)) return GDN_EINVAL;
+    if (states_overlap(*d, live, snap)) return GDN_EALIAS;
+    if ((st = copy_state(*d, live, snap, stream))) return st;
+    snap->pos = live->pos;
+    snap->tag = live->tag;
+    return GDN_OK;
+}
+
+gdn_status gdn_state_restore(const gdn_desc *d, gdn_state *live, const gdn_state *snap,
+                             void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if ((st = check_state(*d, snap))) return st;
+    if (!live || !live->S || (d->conv_width > 0 && !live->conv)) return GDN_EINVAL;
+    if (states_overlap(*d, live, snap)) return GDN_EALIAS;
+    if ((st = copy_state(*d, snap, live, stream))) return st;
+    live->pos = snap->pos;
+    live->tag = snap->tag;
+    return GDN_OK;
+}
+
+gdn_status gdn_state_fork(const gdn_desc *d, const gdn_state *src, gdn_state *dst, int32_t n,
+                          void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if ((st = check_state(*d, src))) return st;
+    if (n < 0 || (n > 0 && !dst)) return GDN_EINVAL;
+    for (int32_t i = 0; i < n; ++i) {
+        if (!dst[i].S || (d->conv_width > 0 && !dst[i].conv)) return GDN_EINVAL;
+        if (states_overlap(*d, src, &dst[i])) return GDN_EALIAS;
+        for (int32_t j = 0; j < i; ++j)
+            if (states_overlap(*d, &dst[i], &dst[j])) return GDN_EALIAS;
+    }
+    for (int32_t i = 0; i < n; ++i) {
+        if ((st = copy_state(*d, src, &dst[i], stream))) return st;
+        dst[i].pos = src->pos;
+        dst[i].tag = src->tag;
+    }
+    return GDN_OK;
+}
+
+gdn_status conv1d_state_step(const gdn_desc *d, const void *x, const void *conv_w, void *window,
+                             void *y, int64_t T, void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (d->conv_width == 0) return GDN_ESHAPE;
+    if (T < 0 || T > INT32_MAX) return GDN_EINVAL;
+    if (!conv_w || !window || (T > 0 && (!x || !y))) return GDN_EINVAL;
+    if (T == 0) return GDN_OK;
+    if (launch_conv_step(*d, x, conv_w, window, y, T, stream) != 0) return GDN_EDEVICE;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_chunked(const gdn_desc *d, const void *x, const void *conv_w,
+                               const float *g, const float *beta, const gdn_state *in,
+                               gdn_state *out, void *o, int64_t T, int32_t mode,
+                               int64_t *rows_done, void *ws, size_t ws_bytes, void *stream)
+{
+    return gdn_prefill_chunked_events(d, x, conv_w, g, beta, in, out, o, T, mode, rows_done, ws,
+                                      ws_bytes, stream, nullptr, 0);
+}
+
+gdn_status gdn_prefill_chunked_events(const gdn_desc *d, const void *x, const void *conv_w,
+                                      const float *g, const float *beta, const gdn_state *in,
+                                      gdn_state *out, void *o, int64_t T, int32_t mode,
+                                      int64_t *rows_done, void *ws, size_t ws_bytes,
+                                      void *stream, void *const *events, int32_t n_events)
+{
+    if (n_events < 0 || (n_events > 0 && !events)) return GDN_EINVAL;
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (mode != GDN_COMMIT && mode != GDN_FORK) return GDN_EINVAL;
+    if (T < 0 || T > INT32_MAX) return GDN_EINVAL;
+    if ((st = check_state(*d, in))) return st;
+    if (!out || !out->S || (d->conv_width > 0 && !out->conv)) return GDN_EINVAL;
+    int64_t n;
+    if (mode == GDN_COMMIT) {
+        if (in->pos % d->grid != 0) return GDN_EGRID;
+        if (!states_same(in, out) && states_overlap(*d, in, out)) return GDN_EALIAS;
+        n = (T / d->grid) * d->grid;
+    } else {
+        if (in->pos % GDN_SUB_CHUNK != 0) return GDN_EGRID;
+        if (states_overlap(*d, in, out)) return GDN_EALIAS;
+        n = T;
+    }
+    if (n > 0) {
+        if (!x || !g || !beta || !o || (d->conv_width > 0 && !conv_w)) return GDN_EINVAL;
+        Seg s;
+        std::memset(&s, 0, sizeof(s));
+        s.row0 = 0;
+        s.n = (int32_t)n;
+        s.S_in = in->S;
+        s.win_in = in->conv;
+        s.S_out = out->S;
+        s.win_out = out->conv;
+        std::vector<Seg> segs(1, s);
+        if (!ws || ws_bytes < workspace_bytes(*d, max_launch_subs(segs))) return GDN_EWORKSPACE;
+        const int64_t pos0 = in->pos;
+        const uint64_t tag = in->tag;
+        if ((st = run_segments(*d, segs, x, conv_w, g, beta, o, ws, stream, events, n_events)))
+            return st;
+        out->pos = pos0 + n;
+        out->tag = tag;
+    } else {
+        if (!states_same(in, out) && (st = copy_state(*d, in, out, stream))) return st;
+        out->pos = in->pos;
+        out->tag = in->tag;
+    }
+    if (rows_done) *rows_done = n;
+    return GDN_OK;
+}
+
+gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_rows,
+                                const void *x, const void *conv_w, const float *g,
+                                const float *beta, const gdn_state *const *init,
+                                gdn_state *const *out, void *o, void *ws, size_t ws_bytes,
+                                void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (B <= 0 || !cu_rows || !init) return GDN_EINVAL;
+    if (cu_rows[0] != 0) return GDN_EINVAL;
+    for (int32_t b = 0; b < B; ++b) {
+        if (cu_rows[b + 1] - cu_rows[b] <= 0) return GDN_EINVAL;  // empty branch
+        if (cu_rows[b + 1] - cu_rows[b] > INT32_MAX) return GDN_EINVAL;
+    }
+    if (!x || !g || !beta || !o || (d->conv_width > 0 && !conv_w)) return GDN_EINVAL;
+    for (int32_t b = 0; b < B; ++b) {
+        if ((st = check_state(*d, init[b]))) return st;
+        if (init[b]->pos % GDN_SUB_CHUNK != 0) return GDN_EGRID;
+    }
+    if (out) {
+        for (int32_t b = 0; b < B; ++b) {
+            if (!out[b] || !out[b]->S || (d->conv_width > 0 && !out[b]->conv)) return GDN_EINVAL;
+            for (int32_t j = 0; j < B; ++j)
+                if (states_overlap(*d, out[b], init[j])) return GDN_EALIAS;
+            for (int32_t j = 0; j < b; ++j)
+                if (states_overlap(*d, out[b], out[j])) return GDN_EALIAS;
+        }
+    }
+    std::vector<Seg> segs((size_t)B);
+    for (int32_t b = 0; b < B; ++b) {
+        Seg &s = segs[b];
+        std::memset(&s, 0, sizeof(s));
+        s.row0 = cu_rows[b];
+        s.n = (int32_t)(cu_rows[b + 1] - cu_rows[b]);
+        s.S_in = init[b]->S;
+        s.win_in = init[b]->conv;
+        // Without requested final states the chain still writes S; it goes to the workspace
+        // tail reserved below.
+        s.S_out = out ? out[b]->S : nullptr;
+        s.win_out = out ? out[b]->conv : nullptr;
+    }
+    const int64_t subs = max_launch_subs(segs);
+    size_t need = workspace_bytes(*d, subs);
+    const size_t s_bytes = gdn_state_S_bytes(d), c_bytes = align256(gdn_state_conv_bytes(d));
+    if (!out) need += (size_t)std::min<int32_t>(B, kMaxSegPerLaunch) * (align256(s_bytes) + c_bytes);
+    if (!ws || ws_bytes < need) return GDN_EWORKSPACE;
+    if (!out) {
+        // scratch final states, reused by every launch group (ordered on the stream)
+        char *tail = (char *)ws + workspace_bytes(*d, subs);
+        for (int32_t b = 0; b < B; ++b) {
+            const int32_t k = b % kMaxSegPerLaunch;
+            segs[b].S_out = (float *)(tail + (size_t)k * (align256(s_bytes) + c_bytes));
+            segs[b].win_out = d->conv_width > 0 ? tail + (size_t)k * (align256(s_bytes) + c_bytes) +
+                                                      align256(s_bytes)
+                                                : nullptr;
+        }
+    }
+    std::vector<int64_t> pos0((size_t)B);
+    for (int32_t b = 0; b < B; ++b) pos0[b] = init[b]->pos;
+    const uint64_t tag = gdn_desc_tag(d);
+    if ((st = run_segments(*d, segs, x, conv_w, g, beta, o, ws, stream))) return st;
+    if (out)
+        for (int32_t b = 0; b < B; ++b) {
+            out[b]->pos = pos0[b] + (cu_rows[b + 1] - cu_rows[b]);
+            out[b]->tag = tag;
+        }
+    return GDN_OK;
+}
+
+int64_t gdn_commit_rows(int64_t n, int32_t grid)
+{
+    if (n < 0 || grid <= 0) return -1;
+    return (n / grid) * grid;
+}
+
+int64_t gdn_shared_prefix_rows(int64_t state_pos, int64_t prefix_end)
+{
+    if (state_pos < 0 || state_pos % GDN_SUB_CHUNK != 0 || prefix_end < state_pos) return -1;
+    const int64_t end = (prefix_end / GDN_SUB_CHUNK) * GDN_SUB_CHUNK;
+    return end > state_pos ? end - state_pos : 0;
+}
+
+gdn_status gdn_ckpt_init(gdn_ckpt_ring *r, int32_t cap)
+{
+    if (!r || cap <= 0 || cap > GDN_MAX_CHECKPOINTS) return GDN_EINVAL;
+    std::memset(r, 0, sizeof(*r));
+    r->cap = cap;
+    for (int i = 0; i < GDN_MAX_CHECKPOINTS; ++i) r->pos[i] = -1;
+    return GDN_OK;
+}
+
+int32_t gdn_ckpt_push(gdn_ckpt_ring *r, int64_t pos)
+{
+    if (!r || r->cap <= 0 || r->cap > GDN_MAX_CHECKPOINTS || pos < 0) return -1;
+    int32_t slot = -1;
+    for (int32_t i = 0; i < r->cap && slot < 0; ++i)
+        if (r->pos[i] == pos) slot = i;
+    for (int32_t i = 0; i < r->cap && slot < 0; ++i)
+        if (r->pos[i] < 0) slot = i;
+    if (slot < 0) {  // evict the oldest
+        slot = 0;
+        for (int32_t i = 1; i < r->cap; ++i)
+            if (r->age[i] < r->age[slot]) slot = i;
+    }
+    if (r->pos[slot] < 0) r->n++;
+    r->pos[slot] = pos;
+    r->age[slot] = ++r->clock;
+    return slot;
+}
+
+int32_t gdn_ckpt_find(const gdn_ckpt_ring *r, int64_t d)
+{
+    if (!r || r->cap <= 0 || r->cap > GDN_MAX_CHECKPOINTS) return -1;
+    int32_t best = -1;
+    for (int32_t i = 0; i < r->cap; ++i)
+        if (r->pos[i] >= 0 && r->pos[i] <= d && (best < 0 || r->pos[i] > r->pos[best])) best = i;
+    return best;
+}
+
+int32_t gdn_ckpt_drop_above(gdn_ckpt_ring *r, int64_t d)
+{
+    if (!r || r->cap <= 0 || r->cap > GDN_MAX_CHECKPOINTS) return 0;
+    int32_t n = 0;
+    for (int32_t i = 0; i < r->cap; ++i)
+        if (r->pos[i] > d) {
+            r->pos[i] = -1;
+            r->age[i] = 0;
+            r->n--;
+            n++;
+        }
+    return n;
+}
+
+const char *gdn_status_str(gdn_status s)
+{
+    switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_EINVAL: return "invalid argument";
+    case GDN_ESHAPE: return "unsupported shape";
+    case GDN_EGRID: return "start position not on the required grid";
+    case GDN_EMISMATCH: return "state tag does not match the descriptor";
+    case GDN_EWORKSPACE: return "workspace missing or too small";
+    case GDN_EDEVICE: return "HIP launch or copy failed";
+    case GDN_EALIAS: return "output state overlaps memory it must not";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// gdn_internal.h -- declarations shared by the host half (gdn_host.cpp) and the kernels
+// (gdn_kernels.hip) of libgdn_prefill.so.  Not part of the public ABI.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// Sequences handled by one launch.  A branch batch with more sequences is cut into
+// launches of at most this many, issued in order on the caller's stream.
+constexpr int kMaxSegPerLaunch = 32;
+constexpr int kC = GDN_SUB_CHUNK;  // 64 rows per sub-chunk
+constexpr int kTileV = 16;         // d_v columns of the state owned by one chain workgroup
+
+// One sequence of a launch: rows [row0, row0 + n) of x / g / beta / o, continued from
+// (S_in, win_in) and finished into (S_out, win_out).  sub0 is the index of its first
+// sub-chunk in the launch's workspace.
+struct Seg {
+    int64_t row0;
+    int32_t n;
+    int32_t sub0;
+    const float *S_in;
+    const void *win_in;
+    float *S_out;
+    void *win_out;
+};
+
+struct SegArgs {
+    int32_t n_seg;
+    int32_t n_sub;  // total sub-chunks of the launch
+    Seg seg[kMaxSegPerLaunch];
+};
+
+// Workspace carved for one launch (device pointers).
+struct Workspace {
+    _Float16 *Qh;  // [n_sub][Hk][64][d]  normalised q, fp16
+    _Float16 *Kh;  // [n_sub][Hk][64][d]  normalised k, fp16
+    _Float16 *Tm;  // [n_sub][Hv][64][64] (I + A)^-1, fp16
+    _Float16 *Mm;  // [n_sub][Hv][64][64] lower(Q K^T) * decay, fp16
+    float *Gc;     // [n_sub][Hv][64]     within-sub-chunk cumulative log decay
+};
+
+size_t workspace_bytes(const gdn_desc &d, int64_t n_sub);
+Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base);
+
+// Launchers (gdn_kernels.hip).  Return 0 or a hipError_t value.
+// events: optional array of 2*n_kernels hipEvent_t recorded around each kernel (may be null).
+int launch_prefill(const gdn_desc &d, const SegArgs &sa, const void *x, const void *conv_w,
+                   const float *g, const float *beta, void *o, const Workspace &ws,
+                   void *stream, void *const *events = nullptr, int n_events = 0);
+int launch_conv_step(const gdn_desc &d, const void *x, const void *conv_w, void *window, void *y,
+                     int64_t T, void *stream);
+int launch_zero(void *p, size_t bytes, void *stream);
+int launch_copy(void *dst, const void *src, size_t bytes, void *stream);
+
+}  // namespace gdn

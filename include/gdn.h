@@ -1,0 +1,229 @@
+/*
+ * gdn.h -- C ABI of libgdn_prefill.so: chunked prefill of one Gated DeltaNet layer on an
+ * AMD Instinct MI355X (gfx950), with a recurrent state that is carried across calls,
+ * committed only on a fixed absolute-position grid, captured, restored and forked.
+ *
+ * Sources of the behaviour (page title, section):
+ *  - "The shadow reader", section "Exact on a grid": the state advances only in whole grid
+ *    chunks at absolute positions k*grid; the rows past the last grid line wait as a
+ *    pending tail; a question runs the tail plus its own rows above the committed rows and
+ *    the state is put back afterwards (a fork); replay equals a fresh prefill bit for bit.
+ *  - "The shadow reader", sections "One session's state" and "Exact on a grid": up to six
+ *    checkpoints, one per turn's prompt end; on a differing prompt go back to the newest
+ *    checkpoint at or below the first differing token, or start over.
+ *  - PR "qwen3_5: run prompts that share prefixes once per prefix", section Purpose: a
+ *    prefix state is the float32 recurrent state plus the last three conv inputs; each
+ *    prefix is run up to its last multiple of 64 rows and the remainder runs with every
+ *    later group or branch; each branch continues from the shared state; invalid requests
+ *    are refused before any device work (section "Test Result").
+ *  - "Long context and sessions", section "Sessions on one engine": states are exported,
+ *    imported and copied between slots; a state made for another layer shape is refused.
+ *
+ * Conventions for every call below:
+ *  - Pointers named "device" point to GPU memory owned by the caller; the library allocates
+ *    no device memory and keeps no pointer after a call returns.  Host pointers likewise.
+ *  - Every argument is validated on the host first.  A negative return means nothing was
+ *    enqueued and no state byte, position or tag changed.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
+ *    returns without synchronising.  GDN_EDEVICE reports a failed launch or copy; the
+ *    outputs are then undefined.
+ *  - The library holds no global mutable state; calls on different streams may overlap as
+ *    long as they write disjoint memory.
+ *
+ * Layouts (row-major, innermost last):
+ *   C   = 2*n_k_heads*d_k + n_v_heads*d_v conv channels, ordered q | k | v, each head's
+ *         dims contiguous; value head h reads key head h / (n_v_heads / n_k_heads).
+ *   x   [T][C]          act dtype  pre-conv inputs (post-conv when conv_width == 0)
+ *   conv_w [C][W]       act dtype  tap W-1 multiplies the current row
+ *   g, beta [T][Hv]     fp32       g <= 0 (log decay), beta in (0,1) (write strength)
+ *   o   [T][Hv][d_v]    out dtype
+ *   S   [Hv][d_k][d_v]  fp32       recurrent state
+ *   conv window [W-1][C] act dtype, oldest row first (the last W-1 conv inputs)
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t gdn_status;
+enum {
+    GDN_OK = 0,
+    GDN_EINVAL = -1,     /* null pointer, bad enum value, negative or empty size */
+    GDN_ESHAPE = -2,     /* head counts / dims / conv width / sub-chunk not supported */
+    GDN_EGRID = -3,      /* a start position is not on the grid the mode requires */
+    GDN_EMISMATCH = -4,  /* a state's tag is not the descriptor's tag */
+    GDN_EWORKSPACE = -5, /* workspace missing or smaller than gdn_workspace_bytes() */
+    GDN_EDEVICE = -6,    /* a HIP launch or copy failed */
+    GDN_EALIAS = -7,     /* an output state overlaps memory it must not */
+};
+
+enum { GDN_F32 = 0, GDN_BF16 = 1 };  /* element types of x / conv / window and of o */
+enum { GDN_COMMIT = 0, GDN_FORK = 1 };
+
+#define GDN_SUB_CHUNK 64 /* the only arithmetic boundary of the chunked form */
+#define GDN_MAX_CHECKPOINTS 6
+
+/* Layer description.  Supported by the kernels: d_k == d_v in {64, 128};
+ * n_v_heads % n_k_heads == 0; conv_width in {0, 4}; sub_chunk == 64;
+ * grid a positive multiple of 64 (512 by default).  scale is the output scale
+ * (d_k^-1/2 usually); l2_eps sits inside the square root of the q/k normalisation. */
+typedef struct {
+    int32_t n_k_heads, n_v_heads, d_k, d_v;
+    int32_t conv_width; /* 4, or 0 = inputs already post-conv */
+    int32_t sub_chunk;  /* must be 64 */
+    int32_t grid;       /* commit grid in rows */
+    int32_t act_dtype;  /* GDN_BF16 or GDN_F32 */
+    int32_t out_dtype;  /* GDN_BF16 or GDN_F32 */
+    int32_t conv_silu;  /* 0 = plain conv, 1 = SiLU after the conv */
+    float scale;
+    float l2_eps;
+} gdn_desc;
+
+/* One recurrent state.  S and conv are device pointers owned by the caller
+ * (conv may be NULL when conv_width == 0).  pos = absolute rows absorbed; tag identifies
+ * the descriptor the state was made for (gdn_desc_tag). */
+typedef struct {
+    float *S;
+    void *conv;
+    int64_t pos;
+    uint64_t tag;
+} gdn_state;
+
+/* ---------------------------------------------------------------- sizes and identity */
+
+/* 0 if the descriptor is supported, else GDN_EINVAL / GDN_ESHAPE. */
+gdn_status gdn_desc_check(const gdn_desc *desc);
+
+/* Tag of a descriptor: a 64-bit FNV-1a hash of the fields that fix a state's meaning
+ * (heads, dims, conv width, sub-chunk, grid, act dtype).  A state is refused by
+ * gdn_state_restore and the prefill calls when its tag differs ("Long context and
+ * sessions", section "Sessions on one engine"; "The shadow reader", section
+ * "Memory and the disk": another grid does not read it). */
+uint64_t gdn_desc_tag(const gdn_desc *desc);
+
+/* Bytes of S ([Hv][d_k][d_v] fp32) and of the conv window ([W-1][C] act dtype). */
+size_t gdn_state_S_bytes(const gdn_desc *desc);
+size_t gdn_state_conv_bytes(const gdn_desc *desc);
+
+/* Device workspace needed by a prefill call of at most max_rows rows in total over at most
+ * max_segments sequences (1 for gdn_prefill_chunked, B for gdn_prefill_branches).
+ * 0 on an invalid descriptor. */
+size_t gdn_workspace_bytes(const gdn_desc *desc, int64_t max_rows, int32_t max_segments);
+
+/* ---------------------------------------------------------------- state operations */
+
+/* Zero S and the window on `stream`; pos = 0; tag = gdn_desc_tag(desc). */
+gdn_status gdn_state_init(const gdn_desc *desc, gdn_state *state, void *stream);
+
+/* snap <- live: device copies of S and the window plus pos and tag.  Refuses a live state
+ * of another tag (GDN_EMISMATCH) and snap == live or overlapping buffers (GDN_EALIAS). */
+gdn_status gdn_state_capture(const gdn_desc *desc, const gdn_state *live, gdn_state *snap,
+                             void *stream);
+
+/* live <- snap.  Refuses a snapshot whose tag is not the descriptor's (GDN_EMISMATCH):
+ * a state for another layer shape or grid is not read. */
+gdn_status gdn_state_restore(const gdn_desc *desc, gdn_state *live, const gdn_state *snap,
+                             void *stream);
+
+/* dst[i] <- src for i in [0, n): n device copies (slots for a batch of branches). */
+gdn_status gdn_state_fork(const gdn_desc *desc, const gdn_state *src, gdn_state *dst, int32_t n,
+                          void *stream);
+
+/* ---------------------------------------------------------------- compute */
+
+/* Standalone causal depthwise conv over all C channels with the window carried:
+ * xt = window ++ x; y[t][c] = sum_j conv_w[c][j] * xt[t+j][c] (SiLU if desc->conv_silu);
+ * the window becomes the last W-1 rows of xt.  y [T][C] in desc->out_dtype (device),
+ * x [T][C] act dtype (device), window [W-1][C] act dtype (device, updated in place).
+ * T >= 0; requires conv_width > 0. */
+gdn_status conv1d_state_step(const gdn_desc *desc, const void *x, const void *conv_w, void *window,
+                             void *y, int64_t T, void *stream);
+
+/* Prefill T rows of one sequence from state `in` into state `out`, writing o.
+ *
+ * GDN_COMMIT: requires in->pos % grid == 0.  Absorbs rows_done = floor(T / grid) * grid
+ *   rows (the rest is the caller's pending tail) and writes o rows [0, rows_done).
+ *   out may equal in (in-place commit); out->pos = in->pos + rows_done.
+ * GDN_FORK: requires in->pos % 64 == 0 and out != in (no overlap).  Absorbs all T rows,
+ *   writes o rows [0, T) and leaves `in` unchanged; out->pos = in->pos + T.
+ *
+ * In both modes the arithmetic boundaries are the absolute multiples of 64 only, so a
+ * replay split into several calls gives the same bits as one call.
+ * x [T][C], g/beta [T][Hv], o [T][Hv][d_v] device; rows_done may be NULL.  ws must hold
+ * gdn_workspace_bytes(desc, T, 1) bytes (device).  Both states' tags must match. */
+gdn_status gdn_prefill_chunked(const gdn_desc *desc, const void *x, const void *conv_w,
+                               const float *g, const float *beta, const gdn_state *in,
+                               gdn_state *out, void *o, int64_t T, int32_t mode,
+                               int64_t *rows_done, void *ws, size_t ws_bytes, void *stream);
+
+/* gdn_prefill_chunked plus per-kernel timing, for benchmarks.  events[0 .. n_events) are
+ * hipEvent_t handles the caller created with timing enabled; the library records
+ * events[2k] before and events[2k+1] after the k-th kernel it enqueues on `stream`
+ * (k = 0 prep, 1 chain, 2 window; pairs past n_events / 2 are not recorded).  Results and
+ * errors are those of gdn_prefill_chunked. */
+gdn_status gdn_prefill_chunked_events(const gdn_desc *desc, const void *x, const void *conv_w,
+                                      const float *g, const float *beta, const gdn_state *in,
+                                      gdn_state *out, void *o, int64_t T, int32_t mode,
+                                      int64_t *rows_done, void *ws, size_t ws_bytes,
+                                      void *stream, void *const *events, int32_t n_events);
+
+/* Batched branch continuation: B sequences packed along rows.  Branch b owns rows
+ * [cu_rows[b], cu_rows[b+1]) of x, g, beta and o (cu_rows is a host array of B+1
+ * non-decreasing offsets starting at 0; every branch has >= 1 row) and starts from
+ * init[b], whose pos must be a multiple of 64.  init entries may repeat (a shared prefix
+ * state, read only).  out may be NULL (no final states), else out[b] receives branch b's
+ * final state; no out[b] may overlap any init state or another out.  ws must hold
+ * gdn_workspace_bytes(desc, cu_rows[B], B) bytes.  Each branch's rows and final state
+ * are bitwise those of a single-sequence gdn_prefill_chunked(GDN_FORK) from init[b]. */
+gdn_status gdn_prefill_branches(const gdn_desc *desc, int32_t B, const int64_t *cu_rows,
+                                const void *x, const void *conv_w, const float *g,
+                                const float *beta, const gdn_state *const *init,
+                                gdn_state *const *out, void *o, void *ws, size_t ws_bytes,
+                                void *stream);
+
+/* ---------------------------------------------------------------- host scheduling (no device) */
+
+/* Rows a COMMIT from an aligned position absorbs out of n available rows:
+ * floor(n / grid) * grid ("The shadow reader", section "Exact on a grid"). -1 on bad args. */
+int64_t gdn_commit_rows(int64_t n, int32_t grid);
+
+/* Rows a shared prefix that ends at absolute row `prefix_end` runs from a state at
+ * `state_pos` (a multiple of 64): max(0, floor(prefix_end / 64) * 64 - state_pos).  The
+ * remaining prefix_end - state_pos - run rows run at the head of every later group or
+ * branch (PR "qwen3_5: run prompts that share prefixes once per prefix", section Purpose,
+ * "Split points").  -1 on bad args. */
+int64_t gdn_shared_prefix_rows(int64_t state_pos, int64_t prefix_end);
+
+/* Checkpoint ring: at most `cap` (<= GDN_MAX_CHECKPOINTS) checkpoints, each at a
+ * committed position, held in caller-owned state slots 0..cap-1 ("The shadow reader",
+ * sections "One session's state" and "Exact on a grid"). */
+typedef struct {
+    int32_t cap, n;
+    int64_t pos[GDN_MAX_CHECKPOINTS];  /* pos[i] of slot i, -1 when empty */
+    uint64_t age[GDN_MAX_CHECKPOINTS]; /* insertion stamp of slot i */
+    uint64_t clock;
+} gdn_ckpt_ring;
+
+gdn_status gdn_ckpt_init(gdn_ckpt_ring *ring, int32_t cap);
+/* Slot to capture a checkpoint at `pos` into: the slot already holding pos, else an empty
+ * slot, else the oldest one (evicted).  Records pos.  -1 on bad args. */
+int32_t gdn_ckpt_push(gdn_ckpt_ring *ring, int64_t pos);
+/* Slot of the newest checkpoint with pos <= d (the largest such pos), or -1 if none:
+ * then start over from a zero state. */
+int32_t gdn_ckpt_find(const gdn_ckpt_ring *ring, int64_t d);
+/* Forget every checkpoint with pos > d (they no longer describe the prompt).  Returns the
+ * number dropped. */
+int32_t gdn_ckpt_drop_above(gdn_ckpt_ring *ring, int64_t d);
+
+/* Static text of a status code. */
+const char *gdn_status_str(gdn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GDN_H */

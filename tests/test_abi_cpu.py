@@ -1,0 +1,231 @@
+"""The C-ABI library on the CPU: exports, validation, grid arithmetic, checkpoint ring.
+
+No compute call runs here: every call below is refused by host validation before any HIP
+call, or is host-only integer logic.  Fake device addresses are never dereferenced.
+"""
+import ctypes
+import itertools
+
+import pytest
+
+from hybrid_linear_attention_prefill_amd import binding as b
+
+FAKE = 0x7F0000000000  # never dereferenced: validation refuses first
+
+
+def layer_desc(**kw):
+    return b.make_desc(16, 32, 128, 128, **kw)
+
+
+def test_every_declared_symbol_is_exported():
+    names = b.exported_names()
+    assert len(names) >= 19
+    for n in names:
+        assert hasattr(b.lib, n), n
+        assert hasattr(b, n) or n in ("gdn_ckpt_init", "gdn_ckpt_push", "gdn_ckpt_find",
+                                      "gdn_ckpt_drop_above"), "binding lacks " + n
+
+
+def test_desc_check_refusals():
+    assert b.gdn_desc_check(layer_desc()) == b.GDN_OK
+    assert b.gdn_desc_check(b.make_desc(1, 1, 64, 64, conv_width=0,
+                                        act_dtype=b.torch.float32)) == b.GDN_OK
+    bad = [
+        (dict(), dict(d_v=64), b.GDN_ESHAPE),          # d_k != d_v
+        (dict(), dict(d_k=96, d_v=96), b.GDN_ESHAPE),  # unsupported head dim
+        (dict(), dict(n_v_heads=24, n_k_heads=16), b.GDN_ESHAPE),
+        (dict(conv_width=3), dict(), b.GDN_ESHAPE),
+        (dict(grid=100), dict(), b.GDN_ESHAPE),
+        (dict(grid=0), dict(), b.GDN_ESHAPE),
+        (dict(sub_chunk=32), dict(), b.GDN_ESHAPE),
+        (dict(), dict(n_k_heads=0), b.GDN_EINVAL),
+    ]
+    for kw, fields, code in bad:
+        d = layer_desc(**kw)
+        for f, v in fields.items():
+            setattr(d, f, v)
+        assert b.gdn_desc_check(d) == code, (kw, fields)
+    d = layer_desc()
+    d.act_dtype = 7
+    assert b.gdn_desc_check(d) == b.GDN_EINVAL
+    assert b.lib.gdn_desc_check(None) == b.GDN_EINVAL
+
+
+def test_tag_identifies_shape_and_grid_not_scale():
+    t = b.gdn_desc_tag(layer_desc())
+    assert t == b.gdn_desc_tag(layer_desc(scale=0.5, l2_eps=1e-3))
+    assert t != b.gdn_desc_tag(layer_desc(grid=1024))
+    assert t != b.gdn_desc_tag(b.make_desc(16, 32, 64, 64))
+    assert t != b.gdn_desc_tag(layer_desc(act_dtype=b.torch.float32))
+
+
+def test_sizes():
+    d = layer_desc()
+    assert b.gdn_state_S_bytes(d) == 32 * 128 * 128 * 4
+    assert b.gdn_state_conv_bytes(d) == 3 * 8192 * 2
+    assert b.gdn_state_conv_bytes(b.make_desc(1, 1, 64, 64, conv_width=0)) == 0
+    w1 = b.gdn_workspace_bytes(d, 8192, 1)
+    w2 = b.gdn_workspace_bytes(d, 8192 + 64, 1)
+    assert 0 < w1 < w2
+    bad = layer_desc(grid=7)
+    assert b.gdn_workspace_bytes(bad, 10, 1) == 0 and b.gdn_state_S_bytes(bad) == 0
+
+
+def _state(pos=0, tag=None, S=FAKE, conv=FAKE + (1 << 30)):
+    s = b.gdn_state(S, conv, pos, b.gdn_desc_tag(layer_desc()) if tag is None else tag)
+    return s
+
+
+def _chunked(d, sin, sout, T=512, mode=b.GDN_COMMIT, ws=FAKE + (2 << 30), ws_bytes=1 << 40,
+             x=FAKE, conv_w=FAKE, g=FAKE, beta=FAKE, o=FAKE):
+    rows = ctypes.c_int64(-7)
+    st = b.lib.gdn_prefill_chunked(ctypes.byref(d), x, conv_w, g, beta, ctypes.byref(sin),
+                                   ctypes.byref(sout), o, T, mode, ctypes.byref(rows), ws,
+                                   ws_bytes, None)
+    return st, rows.value
+
+
+def test_prefill_validation_refuses_before_device_work():
+    d = layer_desc()
+    s = _state(pos=512)
+    before = (s.pos, s.tag)
+    cases = [
+        (dict(sin=_state(pos=100), sout=_state(pos=100)), b.GDN_EGRID),          # commit off grid
+        (dict(sin=_state(pos=32), sout=_state(S=FAKE + (5 << 30), conv=FAKE + (6 << 30)),
+              mode=b.GDN_FORK), b.GDN_EGRID),                                    # fork off 64
+        (dict(sin=s, sout=s, mode=b.GDN_FORK), b.GDN_EALIAS),                    # fork in place
+        (dict(sin=_state(tag=123), sout=_state(tag=123)), b.GDN_EMISMATCH),      # foreign state
+        (dict(sin=s, sout=s, ws=None), b.GDN_EWORKSPACE),
+        (dict(sin=s, sout=s, ws_bytes=1000), b.GDN_EWORKSPACE),
+        (dict(sin=s, sout=s, mode=5), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, T=-1), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, x=None), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, conv_w=None), b.GDN_EINVAL),
+        # overlapping but not identical output state in a commit
+        (dict(sin=s, sout=_state(pos=512, S=FAKE + 64, conv=FAKE + (7 << 30))), b.GDN_EALIAS),
+    ]
+    for kw, code in cases:
+        sin, sout = kw.pop("sin"), kw.pop("sout")
+        pos_in, pos_out = sin.pos, sout.pos
+        st, rows = _chunked(d, sin, sout, **kw)
+        assert st == code, (kw, st)
+        assert rows == -7 and sin.pos == pos_in and sout.pos == pos_out
+    assert (s.pos, s.tag) == before
+
+
+def test_branches_validation():
+    d = layer_desc()
+    s = _state(pos=960)
+    sp = ctypes.pointer(s)
+
+    def call(B, cu, inits, outs=None, ws_bytes=1 << 40):
+        cu_a = (ctypes.c_int64 * len(cu))(*cu)
+        ia = (ctypes.POINTER(b.gdn_state) * B)(*inits)
+        oa = None if outs is None else (ctypes.POINTER(b.gdn_state) * B)(*outs)
+        return b.lib.gdn_prefill_branches(ctypes.byref(d), B, cu_a, FAKE, FAKE, FAKE, FAKE, ia,
+                                          oa, FAKE, FAKE + (3 << 30), ws_bytes, None)
+
+    assert call(2, [0, 10, 10], [sp, sp]) == b.GDN_EINVAL            # empty branch
+    assert call(1, [5, 10], [sp]) == b.GDN_EINVAL                     # offsets must start at 0
+    assert b.lib.gdn_prefill_branches(ctypes.byref(d), 0, None, FAKE, FAKE, FAKE, FAKE, None,
+                                      None, FAKE, FAKE, 1 << 40, None) == b.GDN_EINVAL
+    off = _state(pos=1000)
+    assert call(1, [0, 10], [ctypes.pointer(off)]) == b.GDN_EGRID     # start not on 64
+    assert call(1, [0, 10], [sp], [sp]) == b.GDN_EALIAS               # out overlaps an init
+    o1 = _state(S=FAKE + (8 << 30), conv=FAKE + (9 << 30))
+    assert call(2, [0, 3, 6], [sp, sp], [ctypes.pointer(o1), ctypes.pointer(o1)]) == b.GDN_EALIAS
+    assert call(1, [0, 10], [sp], ws_bytes=10) == b.GDN_EWORKSPACE
+    foreign = _state(pos=0, tag=99)
+    assert call(1, [0, 10], [ctypes.pointer(foreign)]) == b.GDN_EMISMATCH
+
+
+def test_state_ops_validation():
+    d = layer_desc()
+    live = _state(pos=512)
+    other = _state(tag=5, S=FAKE + (10 << 30), conv=FAKE + (11 << 30))
+    assert b.lib.gdn_state_restore(ctypes.byref(d), ctypes.byref(live), ctypes.byref(other),
+                                   None) == b.GDN_EMISMATCH
+    assert live.pos == 512
+    assert b.lib.gdn_state_capture(ctypes.byref(d), ctypes.byref(live), ctypes.byref(live),
+                                   None) == b.GDN_EALIAS
+    assert b.lib.gdn_state_fork(ctypes.byref(d), ctypes.byref(live), None, 2, None) == b.GDN_EINVAL
+    dst = (b.gdn_state * 2)(_state(S=FAKE + (12 << 30), conv=FAKE + (13 << 30)),
+                            _state(S=FAKE + (12 << 30), conv=FAKE + (14 << 30)))
+    assert b.lib.gdn_state_fork(ctypes.byref(d), ctypes.byref(live), dst, 2, None) == b.GDN_EALIAS
+    assert b.lib.conv1d_state_step(ctypes.byref(b.make_desc(1, 1, 64, 64, conv_width=0)), FAKE,
+                                   FAKE, FAKE, FAKE, 10, None) == b.GDN_ESHAPE
+    assert b.lib.conv1d_state_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -1, None) == b.GDN_EINVAL
+    # T == 0 is a no-op that touches nothing
+    assert b.lib.conv1d_state_step(ctypes.byref(d), None, FAKE, FAKE, None, 0, None) == b.GDN_OK
+
+
+def test_commit_rows_exhaustive():
+    for grid in (64, 128, 512, 2048):
+        for n in range(0, 5000, 7):
+            r = b.gdn_commit_rows(n, grid)
+            assert r % grid == 0 and 0 <= n - r < grid
+    assert b.gdn_commit_rows(-1, 512) == -1 and b.gdn_commit_rows(10, 0) == -1
+
+
+def test_shared_prefix_split_rule():
+    """Each prefix runs to its last multiple of 64; the remainder joins every later run."""
+    for P in (0, 1, 63, 64, 65, 300, 1000):
+        run = b.gdn_shared_prefix_rows(0, P)
+        assert run == (P // 64) * 64 and 0 <= P - run < 64
+    # groups of 0/1/70/128 tokens after a 1,000-token request prefix (state at 960)
+    assert [b.gdn_shared_prefix_rows(960, 1000 + gl) for gl in (0, 1, 70, 128)] == [0, 0, 64, 128]
+    for pos in range(0, 1024, 64):
+        for end in range(pos, pos + 300, 5):
+            run = b.gdn_shared_prefix_rows(pos, end)
+            assert run >= 0 and (pos + run) % 64 == 0 and 0 <= end - pos - run
+            assert run == 0 or end - (pos + run) < 64
+    assert b.gdn_shared_prefix_rows(30, 100) == -1 and b.gdn_shared_prefix_rows(64, 10) == -1
+
+
+def test_checkpoint_ring():
+    r = b.CkptRing(6)
+    assert r.find(10 ** 9) == -1                      # none: start over
+    slots = [r.push(p) for p in (512, 1024, 2048, 3072, 4096, 5120)]
+    assert sorted(slots) == list(range(6))
+    assert r.push(1024) == slots[1]                   # same position reuses its slot
+    s = r.push(6144)                                  # full: the oldest (512) is evicted
+    assert s == slots[0] and 512 not in r.positions()
+    assert r.positions()[r.find(3000)] == 2048        # newest at or below the divergence
+    assert r.positions()[r.find(3072)] == 3072
+    assert r.find(1000) == -1                         # 512 was evicted: start over
+    assert r.drop_above(3000) == 4 and max(r.positions()) == 2048  # 3072, 4096, 5120, 6144
+    with pytest.raises(b.GdnError):
+        b.CkptRing(7)
+
+
+def test_checkpoint_ring_matches_brute_force():
+    import random
+    rnd = random.Random(0)
+    for trial in range(200):
+        cap = rnd.randint(1, 6)
+        r = b.CkptRing(cap)
+        model = []  # (pos, stamp)
+        stamp = 0
+        for _ in range(rnd.randint(1, 15)):
+            p = rnd.randrange(0, 20) * 512
+            stamp += 1
+            if any(q == p for q, _ in model):
+                model = [(q, stamp if q == p else t) for q, t in model]
+            elif len(model) < cap:
+                model.append((p, stamp))
+            else:
+                oldest = min(model, key=lambda e: e[1])
+                model.remove(oldest)
+                model.append((p, stamp))
+            r.push(p)
+            for d in range(0, 21 * 512, 256):
+                cands = [q for q, _ in model if q <= d]
+                got = r.find(d)
+                assert (got == -1) == (not cands)
+                if cands:
+                    assert r.positions()[got] == max(cands)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
+        assert isinstance(b.gdn_status_str(code), str) and b.gdn_status_str(code)

@@ -1,0 +1,151 @@
+"""Parity of the HIP path with the float64 oracle, through the C ABI (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_attention_prefill_amd import synth
+from tests.helpers import TOL, new_state, oracle, rel_l2, run_fork, same_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def b():
+    from hybrid_linear_attention_prefill_amd import binding
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return binding
+
+
+def _desc(b, shape, act=torch.bfloat16, out=torch.bfloat16, grid=512, **kw):
+    return b.make_desc(shape.n_k_heads, shape.n_v_heads, shape.d_k, shape.d_v,
+                       conv_width=shape.conv_width, grid=grid, act_dtype=act, out_dtype=out, **kw)
+
+
+def _check_parity(o_gpu, S_gpu, o_ref, S_ref, heads=None, tol=TOL):
+    o = o_gpu.float().cpu().numpy()
+    S = S_gpu.cpu().numpy()
+    if heads is not None:
+        o, S, o_ref, S_ref = o[:, heads], S[heads], o_ref[:, heads], S_ref[heads]
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    print("rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+def test_one_head_fp32(b):
+    """One value head, d=64, T=1024, fp32 in and out, inputs already post-conv."""
+    d = _desc(b, synth.ONE_HEAD, act=torch.float32, out=torch.float32)
+    inp = synth.layer_inputs(synth.ONE_HEAD, 1024, seed=0, act_dtype=torch.float32, unit_qk=True)
+    dinp = to_dev(inp)
+    s0 = new_state(b, d)
+    o, s1 = run_fork(b, d, dinp, s0)
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle(d, inp)
+    eo, es = _check_parity(o, s1.S, o_ref, S_ref)
+    assert s1.pos == 1024
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 300])
+def test_layer_small_all_heads(b, T):
+    """16/32 heads, d=128, conv, bf16: several sub-chunks and ragged tails, every head."""
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape)
+    inp = synth.layer_inputs(shape, T, seed=1)
+    dinp = to_dev(inp)
+    o, s1 = run_fork(b, d, dinp, new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, w_ref = oracle(d, inp)
+    _check_parity(o, s1.S, o_ref, S_ref)
+    assert np.array_equal(synth.f64(s1.conv), w_ref)
+
+
+def test_layer_fp32_out_tighter(b):
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape, out=torch.float32)
+    inp = synth.layer_inputs(shape, 256, seed=2)
+    dinp = to_dev(inp)
+    o, s1 = run_fork(b, d, dinp, new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle(d, inp)
+    eo, es = _check_parity(o, s1.S, o_ref, S_ref)
+    assert eo < 1e-3
+
+
+def test_layer_d64(b):
+    shape = synth.Shape(2, 4, 64, 64, 4)
+    d = _desc(b, shape)
+    inp = synth.layer_inputs(shape, 200, seed=3)
+    o, s1 = run_fork(b, d, to_dev(inp), new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle(d, inp)
+    _check_parity(o, s1.S, o_ref, S_ref)
+
+
+def test_slow_decay_stress(b):
+    """g scaled by 0.01 (beyond the stated inputs): the state carries across sub-chunks."""
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape, out=torch.float32)
+    inp = synth.layer_inputs(shape, 512, seed=4, g_scale=0.01)
+    o, s1 = run_fork(b, d, to_dev(inp), new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, _ = oracle(d, inp)
+    _check_parity(o, s1.S, o_ref, S_ref)
+
+
+def test_nonzero_initial_state_and_window(b):
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape)
+    pre = synth.layer_inputs(shape, 128 + 77, seed=5)
+    dpre = to_dev(pre)
+    # build a state by a first FORK of 128 rows, then continue with 77 rows
+    _, s1 = run_fork(b, d, dpre, new_state(b, d), rows=(0, 128))
+    o2, s2 = run_fork(b, d, dpre, s1, rows=(128, 205))
+    torch.cuda.synchronize()
+    S1 = s1.S.cpu().numpy().astype(np.float64)
+    W1 = synth.f64(s1.conv)
+    part = {k: v[128:205] for k, v in pre.items() if k != "conv_w"}
+    part["conv_w"] = pre["conv_w"]
+    o_ref, S_ref, w_ref = oracle(d, part, S0=S1, window=W1)
+    _check_parity(o2, s2.S, o_ref, S_ref)
+    assert np.array_equal(synth.f64(s2.conv), w_ref)
+
+
+def test_full_layer_8192_sampled_heads(b):
+    """The 16/32/128 layer at T=8192 in one call; the oracle runs only sampled value heads."""
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape)
+    inp = synth.layer_inputs(shape, 8192, seed=0)
+    o, s1 = run_fork(b, d, to_dev(inp), new_state(b, d))
+    torch.cuda.synchronize()
+    heads = [0, 13, 31]
+    o_ref, S_ref, w_ref = oracle(d, inp, heads=heads)
+    _check_parity(o, s1.S, o_ref, S_ref, heads=heads)
+    assert np.array_equal(synth.f64(s1.conv), w_ref)
+
+
+def test_deterministic_repeat(b):
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape)
+    dinp = to_dev(synth.layer_inputs(shape, 1000, seed=6))
+    o1, s1 = run_fork(b, d, dinp, new_state(b, d))
+    o2, s2 = run_fork(b, d, dinp, new_state(b, d))
+    torch.cuda.synchronize()
+    assert same_bits(o1, o2) and same_bits(s1.S, s2.S) and same_bits(s1.conv, s2.conv)
+
+
+def test_conv1d_state_step(b):
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape, out=torch.float32)
+    inp = synth.layer_inputs(shape, 70, seed=7)
+    from oracle import c_oracle
+    rng = np.random.default_rng(0)
+    win0 = synth.cast(rng.standard_normal((3, shape.channels)), torch.bfloat16)
+    window = win0.cuda()
+    y = torch.empty((70, shape.channels), dtype=torch.float32, device="cuda")
+    b.conv1d_state_step(d, inp["x"].cuda(), inp["conv_w"].cuda(), window, y)
+    torch.cuda.synchronize()
+    y_ref, w_ref = c_oracle.causal_conv(synth.f64(inp["x"]), synth.f64(inp["conv_w"]),
+                                        synth.f64(win0))
+    assert rel_l2(y.cpu().numpy(), y_ref) < 1e-6
+    assert np.array_equal(synth.f64(window), w_ref)
