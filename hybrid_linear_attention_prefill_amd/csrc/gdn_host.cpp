@@ -25,22 +25,22 @@ static size_t out_size(const gdn_desc &d) { return d.out_dtype == GDN_BF16 ? 2 :
 size_t workspace_bytes(const gdn_desc &d, int64_t n_sub)
 {
     const size_t qk = align256((size_t)n_sub * d.n_k_heads * kC * d.d_k * 2);
-    const size_t tm = align256((size_t)n_sub * d.n_v_heads * kC * kC * 2);
-    const size_t gc = align256((size_t)n_sub * d.n_v_heads * kC * 4);
+    const size_t tm = align256((size_t)n_sub * d.n_v_heads * kPackedTri * 2);
+    const size_t gc = align256((size_t)n_sub * d.n_v_heads * 4 * kC * 4);
     return 2 * qk + 2 * tm + gc;
 }
 
 Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base)
 {
     const size_t qk = align256((size_t)n_sub * d.n_k_heads * kC * d.d_k * 2);
-    const size_t tm = align256((size_t)n_sub * d.n_v_heads * kC * kC * 2);
+    const size_t tm = align256((size_t)n_sub * d.n_v_heads * kPackedTri * 2);
     char *p = (char *)base;
     Workspace w;
     w.Qh = (_Float16 *)p;
     w.Kh = (_Float16 *)(p + qk);
     w.Tm = (_Float16 *)(p + 2 * qk);
     w.Mm = (_Float16 *)(p + 2 * qk + tm);
-    w.Gc = (float *)(p + 2 * qk + 2 * tm);
+    w.Fac = (float *)(p + 2 * qk + 2 * tm);
     return w;
 }
 

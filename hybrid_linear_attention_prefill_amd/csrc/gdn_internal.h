@@ -13,6 +13,7 @@ namespace gdn {
 constexpr int kMaxSegPerLaunch = 32;
 constexpr int kC = GDN_SUB_CHUNK;  // 64 rows per sub-chunk
 constexpr int kTileV = 16;         // d_v columns of the state owned by one chain workgroup
+constexpr int kPackedTri = 10 * 256;  // fp16 values of a packed lower-triangular 64x64 factor
 
 // One sequence of a launch: rows [row0, row0 + n) of x / g / beta / o, continued from
 // (S_in, win_in) and finished into (S_out, win_out).  sub0 is the index of its first
@@ -37,9 +38,9 @@ struct SegArgs {
 struct Workspace {
     _Float16 *Qh;  // [n_sub][Hk][64][d]  normalised q, fp16
     _Float16 *Kh;  // [n_sub][Hk][64][d]  normalised k, fp16
-    _Float16 *Tm;  // [n_sub][Hv][64][64] (I + A)^-1, fp16
-    _Float16 *Mm;  // [n_sub][Hv][64][64] lower(Q K^T) * decay, fp16
-    float *Gc;     // [n_sub][Hv][64]     within-sub-chunk cumulative log decay
+    _Float16 *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1, packed lower 16x16 tiles, fp16
+    _Float16 *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay, packed likewise
+    float *Fac;    // [n_sub][Hv][4][64]  per row: beta, beta*gamma, gamma, exp(G_n - G) (fp32)
 };
 
 size_t workspace_bytes(const gdn_desc &d, int64_t n_sub);
