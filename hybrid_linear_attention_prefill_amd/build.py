@@ -16,7 +16,9 @@ SOURCES = [os.path.join(PKG, "csrc", "gdn_host.cpp"), os.path.join(PKG, "csrc", 
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is switched off for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # keep MFMA accumulators in ordinary VGPRs (fewer accumulator-register moves)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc():

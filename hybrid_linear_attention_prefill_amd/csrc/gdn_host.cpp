@@ -125,6 +125,17 @@ static gdn_status run_segments(const gdn_desc &d, const std::vector<Seg> &segs, 
     return GDN_OK;
 }
 
+// Rows of one sequence per launch: the chain kernel addresses x and o of a sequence with 32-bit
+// byte offsets, so a longer sequence is run as several chained launches, each starting at a
+// multiple of 64 rows (which changes no bit of the result).
+static int64_t max_rows_per_launch(const gdn_desc &d)
+{
+    const int64_t row_bytes = std::max<int64_t>(n_channels(d) * (int64_t)act_size(d),
+                                                (int64_t)d.n_v_heads * d.d_v * (int64_t)out_size(d));
+    const int64_t rows = ((int64_t)INT32_MAX - 4 * row_bytes) / row_bytes;
+    return (rows / kC) * kC;
+}
+
 // Largest per-launch sub-chunk count of `segs`.
 static int64_t max_launch_subs(const std::vector<Seg> &segs)
 {
@@ -302,20 +313,25 @@ gdn_status gdn_prefill_chunked_events(const gdn_desc *d, const void *x, const vo
     }
     if (n > 0) {
         if (!x || !g || !beta || !o || (d->conv_width > 0 && !conv_w)) return GDN_EINVAL;
-        Seg s;
-        std::memset(&s, 0, sizeof(s));
-        s.row0 = 0;
-        s.n = (int32_t)n;
-        s.S_in = in->S;
-        s.win_in = in->conv;
-        s.S_out = out->S;
-        s.win_out = out->conv;
-        std::vector<Seg> segs(1, s);
-        if (!ws || ws_bytes < workspace_bytes(*d, max_launch_subs(segs))) return GDN_EWORKSPACE;
+        const int64_t piece = max_rows_per_launch(*d);
+        if (!ws || ws_bytes < workspace_bytes(*d, (std::min(n, piece) + kC - 1) / kC))
+            return GDN_EWORKSPACE;
         const int64_t pos0 = in->pos;
         const uint64_t tag = in->tag;
-        if ((st = run_segments(*d, segs, x, conv_w, g, beta, o, ws, stream, events, n_events)))
-            return st;
+        for (int64_t r0 = 0; r0 < n; r0 += piece) {
+            Seg s;
+            std::memset(&s, 0, sizeof(s));
+            s.row0 = r0;
+            s.n = (int32_t)std::min(piece, n - r0);
+            s.S_in = r0 == 0 ? in->S : out->S;
+            s.win_in = r0 == 0 ? in->conv : out->conv;
+            s.S_out = out->S;
+            s.win_out = out->conv;
+            std::vector<Seg> segs(1, s);
+            if ((st = run_segments(*d, segs, x, conv_w, g, beta, o, ws, stream,
+                                   r0 == 0 ? events : nullptr, r0 == 0 ? n_events : 0)))
+                return st;
+        }
         out->pos = pos0 + n;
         out->tag = tag;
     } else {
@@ -339,7 +355,7 @@ gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_
     if (cu_rows[0] != 0) return GDN_EINVAL;
     for (int32_t b = 0; b < B; ++b) {
         if (cu_rows[b + 1] - cu_rows[b] <= 0) return GDN_EINVAL;  // empty branch
-        if (cu_rows[b + 1] - cu_rows[b] > INT32_MAX) return GDN_EINVAL;
+        if (cu_rows[b + 1] - cu_rows[b] > max_rows_per_launch(*d)) return GDN_ESHAPE;
     }
     if (!x || !g || !beta || !o || (d->conv_width > 0 && !conv_w)) return GDN_EINVAL;
     for (int32_t b = 0; b < B; ++b) {

@@ -13,7 +13,11 @@ namespace gdn {
 constexpr int kMaxSegPerLaunch = 32;
 constexpr int kC = GDN_SUB_CHUNK;  // 64 rows per sub-chunk
 constexpr int kTileV = 16;         // d_v columns of the state owned by one chain workgroup
-constexpr int kPackedTri = 10 * 256;  // fp16 values of a packed lower-triangular 64x64 factor
+// A lower-triangular 64x64 factor (Tinv or M) is stored as the MFMA A fragments that the chain
+// kernel's waves load: (row tile w, 32-wide K step kb) for (0,0) (1,0) (2,0) (2,1) (3,0) (3,1),
+// each 64 lanes x 8 fp16 (lane l: row 16w + l%16, columns 32kb + 8(l/16) .. +7).
+constexpr int kTriFrags = 6;
+constexpr int kPackedTri = kTriFrags * 64 * 8;
 
 // One sequence of a launch: rows [row0, row0 + n) of x / g / beta / o, continued from
 // (S_in, win_in) and finished into (S_out, win_out).  sub0 is the index of its first
@@ -36,10 +40,11 @@ struct SegArgs {
 
 // Workspace carved for one launch (device pointers).
 struct Workspace {
-    _Float16 *Qh;  // [n_sub][Hk][64][d]  normalised q, fp16
-    _Float16 *Kh;  // [n_sub][Hk][64][d]  normalised k, fp16
-    _Float16 *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1, packed lower 16x16 tiles, fp16
-    _Float16 *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay, packed likewise
+    _Float16 *Qh;  // [n_sub][Hk][64*d]  normalised q, fp16, in MFMA A-fragment order
+    _Float16 *Kh;  // [n_sub][Hk][64*d]  normalised k, likewise: fragment (w, kb) lane l holds
+                   //                    row 16w + l%16, columns 32kb + 8(l/16) .. +7
+    _Float16 *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1 fragments, fp16
+    _Float16 *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay fragments, fp16
     float *Fac;    // [n_sub][Hv][4][64]  per row: beta, beta*gamma, gamma, exp(G_n - G) (fp32)
 };
 

@@ -62,13 +62,24 @@ __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint
 
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-    u += 0x7fffu + ((u >> 16) & 1u);                                           // nearest even
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);  // v_cvt_pk_bf16_f32: round to nearest even
 }
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t *p, float v) { p->bits = f32_to_bf16_bits(v); }
+
+// Store one output element at element offset `off` of a raw buffer (dropped out of range).
+template <typename Out>
+__device__ __forceinline__ void store_out_buf(__amdgpu_buffer_rsrc_t r, int off, float v);
+template <>
+__device__ __forceinline__ void store_out_buf<float>(__amdgpu_buffer_rsrc_t r, int off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off * 4, 0, 0);
+}
+template <>
+__device__ __forceinline__ void store_out_buf<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, float v)
+{
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, off * 2, 0, 0);
+}
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
 {
@@ -102,14 +113,9 @@ __device__ __forceinline__ int find_seg(const SegArgs &sa, int sub)
     return s;
 }
 
-// Packed lower-triangular 64x64 factors (Tinv and M): the 10 tiles (i, j <= i) of 16x16 in
-// the order (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3); inside a tile the
-// 256 values sit in MFMA accumulator order: element (r, c) at (r % 4) * 64 + (r / 4) * 16 + c,
-// so 16-byte chunk q holds row 4 ((q % 8) / 2) + q / 8, columns (q % 2) * 8 .. + 7.
-__device__ __forceinline__ int tile_i(int p) { return p < 1 ? 0 : p < 3 ? 1 : p < 6 ? 2 : 3; }
-__device__ __forceinline__ int tile_j(int p) { return p - tile_i(p) * (tile_i(p) + 1) / 2; }
-__device__ __forceinline__ int chunk_row(int q) { return 4 * ((q % 8) / 2) + q / 8; }
-__device__ __forceinline__ int chunk_col(int q) { return (q % 2) * 8; }
+// Fragment (w, kb) of a lower-triangular factor: its index among the stored ones, or -1 when
+// every column of the K step lies above the diagonal of row tile w (the fragment is zero).
+__device__ __forceinline__ int tri_frag(int w, int kb) { return kb == 0 ? (w < 2 ? w : 2 * w - 2) : (w < 2 ? -1 : 2 * w - 1); }
 
 template <typename Act>
 __device__ __forceinline__ void load8(const u32x4 *row, int cl, float (&v)[8])
@@ -134,10 +140,10 @@ __device__ __forceinline__ void load8(const u32x4 *row, int cl, float (&v)[8])
 // ------------------------------------------------------------------------------------------
 // prep_kernel: state-independent factors of one (sub-chunk, key head).
 // ------------------------------------------------------------------------------------------
-template <int D, typename Act>
+template <int D, typename Act, bool SILU>
 __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__restrict__ x,
                                                       const Act *__restrict__ conv_w, int conv_on,
-                                                      int silu, const float *__restrict__ g,
+                                                      const float *__restrict__ g,
                                                       const float *__restrict__ beta, int Hk,
                                                       int Hv, float eps, Workspace ws)
 {
@@ -207,13 +213,19 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
         const int cg = tid % G8, rp = tid / G8;
         const int cl = cg * 8, part = cl / D, cd = cl % D;
         const int ch0 = part * Hk * D + kh * D + cd;
-        float w[8][4];
+        float w[8][4];  // taps of channels ch0 .. ch0+7: 32 consecutive values of conv_w
+        {
+            u32x4 wc[8 * (int)sizeof(Act) / 4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
+            for (int q = 0; q < 8 * (int)sizeof(Act) / 4; ++q)
+                wc[q] = conv_on ? ((const u32x4 *)(conv_w + ch0 * 4))[q] : u32x4{0u, 0u, 0u, 0u};
+            const Act *wv = (const Act *)wc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w[e][j] = conv_on ? to_f32(conv_w[(ch0 + e) * 4 + j]) : 0.f;
+            for (int e = 0; e < 8; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) w[e][j] = to_f32(wv[e * 4 + j]);
+        }
         _Float16 *dstl = part ? k16 : q16;
-        _Float16 *dstg = (part ? ws.Kh : ws.Qh) + ((int64_t)sub * Hk + kh) * kC * D;
 #pragma unroll
         for (int ri = 0; ri < RPT; ++ri) {
             const int r = rp * RPT + ri;
@@ -226,7 +238,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
                 for (int e = 0; e < 8; ++e) {
                     float a = w[e][0] * xv[0][e] + w[e][1] * xv[1][e] + w[e][2] * xv[2][e] +
                               w[e][3] * xv[3][e];
-                    if (silu) a = a / (1.f + expf(-a));
+                    if constexpr (SILU) a = a / (1.f + expf(-a));
                     y[e] = a;
                 }
             } else {
@@ -242,10 +254,21 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
 #pragma unroll
             for (int e = 0; e < 8; ++e) hv[e] = (_Float16)(y[e] * inv);
             *(half8 *)(dstl + r * HS + cd) = hv;
-            *(half8 *)(dstg + r * D + cd) = hv;
         }
     }
     __syncthreads();
+
+    // normalised q, k to the workspace in MFMA A-fragment order (coalesced for the chain)
+    {
+        _Float16 *Qg = ws.Qh + ((int64_t)sub * Hk + kh) * kC * D;
+        _Float16 *Kg = ws.Kh + ((int64_t)sub * Hk + kh) * kC * D;
+        for (int c = tid; c < kC * D / 8; c += 256) {
+            const int f = c / 64, l = c % 64, w = f / (D / 32), kb = f % (D / 32);
+            const int off = (16 * w + l % 16) * HS + 32 * kb + 8 * (l / 16);
+            *(half8 *)(Qg + c * 8) = *(const half8 *)(q16 + off);
+            *(half8 *)(Kg + c * 8) = *(const half8 *)(k16 + off);
+        }
+    }
 
     // 3. K K^T and Q K^T, row tile `wave`, column tiles j <= wave
     f32x4 kk[4], qk[4];
@@ -291,12 +314,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
         }
         __syncthreads();
 
-        // A into LDS (fp32, zeros on and above the diagonal), M packed into the workspace
+        // A into LDS (fp32, zeros on and above the diagonal); M stays in registers for now
+        f32x4 mreg[4];
         {
-            _Float16 *Mg = ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                half4 mv;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * wave + 4 * (lane / 16) + i, c = 16 * j + lane % 16;
@@ -307,12 +329,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
                         if (c < r) a = bs[r] * kk[j][i] * dec;
                     }
                     As[r * AS + c] = a;
-                    mv[i] = (_Float16)m;
-                }
-                if (j <= wave) {
-                    const int p = wave * (wave + 1) / 2 + j;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) Mg[p * 256 + i * 64 + lane] = mv[i];
+                    mreg[j][i] = m;
                 }
             }
         }
@@ -366,201 +383,247 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             }
             __syncthreads();
         }
-        // Tinv packed into the workspace (fp16)
+        // M into LDS over A (no longer needed), then Tinv and M to the workspace as fragments
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                As[(16 * wave + 4 * (lane / 16) + i) * AS + 16 * j + lane % 16] = mreg[j][i];
+        __syncthreads();
         {
             _Float16 *Tg = ws.Tm + ((int64_t)sub * Hv + h) * kPackedTri;
-            for (int idx = tid; idx < 10 * 32; idx += 256) {
-                const int p = idx / 32, q = idx % 32;
-                const float *src = Ts + (16 * tile_i(p) + chunk_row(q)) * AS + 16 * tile_j(p) + chunk_col(q);
+            _Float16 *Mg = ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
+            for (int c = tid; c < 2 * kTriFrags * 64; c += 256) {
+                const int which = c / (kTriFrags * 64), cf = c % (kTriFrags * 64);
+                const int f = cf / 64, l = cf % 64;
+                const int w = f < 2 ? f : 2 + (f - 2) / 2, kb = f < 2 ? 0 : (f - 2) % 2;
+                const float *src = (which ? As : Ts) + (16 * w + l % 16) * AS + 32 * kb + 8 * (l / 16);
                 half8 hv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) hv[e] = (_Float16)src[e];
-                *(half8 *)(Tg + p * 256 + q * 8) = hv;
+                *(half8 *)((which ? Mg : Tg) + cf * 8) = hv;
             }
         }
         __syncthreads();
     }
 }
 
-// One sub-chunk's chain inputs as staged in a loader thread's registers: K, Q, packed Tinv and
-// M, raw v rows of this workgroup's 16 columns (with the 3 halo rows), and the factor table.
-constexpr int kLoaders = 512;  // loader threads of a chain workgroup (waves 4..11)
-
+// Per-lane register set of one sub-chunk's chain inputs.  Compute wave w handles rows
+// 16w .. 16w+15: its MFMA A fragments of K, Q, Tinv and M come straight into registers.  Each
+// thread also carries LP 16-byte chunks bound for LDS: first the raw v rows of this
+// workgroup's 16 columns (3 halo rows + 64), then the 1 KB factor table.
 template <int D, typename Act>
-struct LoadSet {
-    static constexpr int QKP = kC * D / 8 / kLoaders;  // 16-byte chunks of K (and Q) per thread
-    static constexpr int TMC = 10 * 32;                // chunks of packed Tinv (and of M)
-    static constexpr int TMP = (TMC + kLoaders - 1) / kLoaders;
+struct StepRegs {
+    static constexpr int KB = D / 32;                  // 32-wide K steps over d_k
     static constexpr int EPC = 16 / (int)sizeof(Act);
     static constexpr int VCR = 16 / EPC;               // chunks per v row (16 values)
-    static constexpr int VC = (kC + 3) * VCR;
-    static constexpr int VP = (VC + kLoaders - 1) / kLoaders;
-    u32x4 k[QKP], q[QKP], t[TMP], m[TMP], v[VP], f;
+    static constexpr int VC = (kC + 3) * VCR;          // v chunks
+    static constexpr int NLD = VC + 64;                // + factor table chunks
+    static constexpr int LP = (NLD + 255) / 256;       // LDS-bound chunks per thread
+    half8 kf[KB], qf[KB], tf[2], mf[2];
+    u32x4 ld[LP];
 };
 
 struct ChainArgs {
-    int sub0, seg_n, kh, h, Hk, Hv, C, vch, conv_on, c0;
+    int sub0, seg_n, kh, h, Hk, Hv, C, vch, conv_on, c0, wave, col, kg, tid;
     int64_t seg_row0;
+    // Buffer resources: their range checks return 0 for reads outside the sequence (rows past
+    // its end or before its start) and drop writes outside it, so loads and stores need no
+    // branches.
+    __amdgpu_buffer_rsrc_t rx;  // x rows of the sequence, from its first row
+    __amdgpu_buffer_rsrc_t ro;  // o rows of the sequence
 };
 
-// Loader side: issue the global loads of sub-chunk `cl` into `ls`.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
 template <int D, typename Act>
-__device__ __forceinline__ void load_issue(LoadSet<D, Act> &ls, const ChainArgs &a, int lt, int cl,
-                                           const Act *__restrict__ x, const Act *win,
+__device__ __forceinline__ void step_issue(StepRegs<D, Act> &R, const ChainArgs &a, int cl,
                                            const Workspace &ws)
 {
-    using L = LoadSet<D, Act>;
+    using SR = StepRegs<D, Act>;
     const int sub = a.sub0 + cl, rb = cl * kC;
-    const u32x4 *Kg = (const u32x4 *)(ws.Kh + ((int64_t)sub * a.Hk + a.kh) * kC * D);
-    const u32x4 *Qg = (const u32x4 *)(ws.Qh + ((int64_t)sub * a.Hk + a.kh) * kC * D);
+    const int lane = 16 * a.kg + a.col;
+    const half8 *Kg = (const half8 *)(ws.Kh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
+    const half8 *Qg = (const half8 *)(ws.Qh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
 #pragma unroll
-    for (int i = 0; i < L::QKP; ++i) {
-        ls.k[i] = Kg[lt + kLoaders * i];
-        ls.q[i] = Qg[lt + kLoaders * i];
+    for (int kb = 0; kb < SR::KB; ++kb) {
+        R.kf[kb] = Kg[kb * 64];
+        R.qf[kb] = Qg[kb * 64];
     }
-    const u32x4 *Tg = (const u32x4 *)(ws.Tm + ((int64_t)sub * a.Hv + a.h) * kPackedTri);
-    const u32x4 *Mg = (const u32x4 *)(ws.Mm + ((int64_t)sub * a.Hv + a.h) * kPackedTri);
+    const half8 *Tg = (const half8 *)(ws.Tm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
+    const half8 *Mg = (const half8 *)(ws.Mm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
+    const half8 z = {};
+    R.tf[0] = Tg[64 * tri_frag(a.wave, 0)];
+    R.mf[0] = Mg[64 * tri_frag(a.wave, 0)];
+    if (a.wave >= 2) {  // wave-uniform
+        R.tf[1] = Tg[64 * tri_frag(a.wave, 1)];
+        R.mf[1] = Mg[64 * tri_frag(a.wave, 1)];
+    } else {
+        R.tf[1] = z;
+        R.mf[1] = z;
+    }
+    const u32x4 *Fg = (const u32x4 *)(ws.Fac + ((int64_t)sub * a.Hv + a.h) * 4 * kC);
 #pragma unroll
-    for (int i = 0; i < L::TMP; ++i) {
-        const int idx = lt + kLoaders * i;
-        ls.t[i] = u32x4{0u, 0u, 0u, 0u};
-        ls.m[i] = u32x4{0u, 0u, 0u, 0u};
-        if (idx < L::TMC) {
-            ls.t[i] = Tg[idx];
-            ls.m[i] = Mg[idx];
+    for (int i = 0; i < SR::LP; ++i) {
+        const int idx = a.tid + 256 * i;
+        if (idx < SR::VC) {
+            const int vr = idx / SR::VCR, cc = (idx % SR::VCR) * SR::EPC;
+            const int sr = rb + vr - 3;  // sequence-local row (rows before 0: the window, added apart)
+            R.ld[i] = __builtin_amdgcn_raw_buffer_load_b128(a.rx, (sr * a.C + a.vch + cc) * (int)sizeof(Act), 0, 0);
+        } else {
+            R.ld[i] = Fg[min(idx - SR::VC, 63)];
         }
     }
-#pragma unroll
-    for (int i = 0; i < L::VP; ++i) {
-        const int idx = lt + kLoaders * i;
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (idx < L::VC) {
-            const int row = idx / L::VCR, cc = (idx % L::VCR) * L::EPC;
-            const int sr = rb + row - 3;
-            if (sr < 0) {
-                if (a.conv_on) v = *(const u32x4 *)(win + (int64_t)(3 + sr) * a.C + a.vch + cc);
-            } else if (sr < a.seg_n) {
-                v = *(const u32x4 *)(x + (a.seg_row0 + sr) * a.C + a.vch + cc);
-            }
-        }
-        ls.v[i] = v;
-    }
-    ls.f = u32x4{0u, 0u, 0u, 0u};
-    if (lt < 64) ls.f = ((const u32x4 *)(ws.Fac + ((int64_t)sub * a.Hv + a.h) * 4 * kC))[lt];
 }
 
-// LDS of the chain kernel.  K, M and the factor table are double-buffered (read after the
-// second barrier of a step while the next step's copy is written); Q, Tinv and the v rows are
-// single (their last reader precedes the barrier after which the loader overwrites them).
-template <int D, typename Act, typename Out>
+// LDS of the chain kernel: K of the current sub-chunk (for the transposed reads of the state
+// update), the raw v rows, the factor tables (double-buffered), S^T as the fp16 MFMA operand,
+// and the transposed 64 x 16 tiles.
+template <int D, typename Act>
 struct ChainLds {
     static constexpr int HS = D + 8, TS = kC + 8, ST = D + 8;
-    _Float16 k16[2][kC * HS];
-    _Float16 q16[kC * HS];
-    _Float16 t16[kC * TS];
-    _Float16 m16[2][kC * TS];
+    _Float16 k16[kC * HS];
     _Float16 s16t[16 * ST];
     _Float16 rt[16 * TS], dt[16 * TS], ddt[16 * TS];
-    float fac[2][4 * kC];
-    u32x4 xvr[LoadSet<D, Act>::VC];
-    Out obuf[kC * 16];
+    u32x4 xvr[StepRegs<D, Act>::VC];
+    float fac[2][4 * kC];  // per row: beta, beta*gamma, gamma, exp(G_n - G)
 };
 
-template <int D, typename Act, typename Out>
-__device__ __forceinline__ void load_put_early(ChainLds<D, Act, Out> &L, const LoadSet<D, Act> &ls,
-                                               int lt, int buf)
+template <int D, typename Act>
+__device__ __forceinline__ void put_ld(ChainLds<D, Act> &L, const StepRegs<D, Act> &R, int tid, int buf)
 {
-    using LS = LoadSet<D, Act>;
-    constexpr int HS = ChainLds<D, Act, Out>::HS, TS = ChainLds<D, Act, Out>::TS;
+    using SR = StepRegs<D, Act>;
 #pragma unroll
-    for (int i = 0; i < LS::QKP; ++i) {
-        const int idx = lt + kLoaders * i, r = idx / (D / 8), cc = (idx % (D / 8)) * 8;
-        *(u32x4 *)(L.k16[buf] + r * HS + cc) = ls.k[i];
-        *(u32x4 *)(L.q16 + r * HS + cc) = ls.q[i];
-    }
-#pragma unroll
-    for (int i = 0; i < LS::TMP; ++i) {
-        const int idx = lt + kLoaders * i;
-        if (idx < LS::TMC) {
-            const int p = idx / 32, q = idx % 32;
-            *(u32x4 *)(L.m16[buf] + (16 * tile_i(p) + chunk_row(q)) * TS + 16 * tile_j(p) +
-                       chunk_col(q)) = ls.m[i];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < LS::VP; ++i) {
-        const int idx = lt + kLoaders * i;
-        if (idx < LS::VC) L.xvr[idx] = ls.v[i];
-    }
-    if (lt < 64) ((u32x4 *)L.fac[buf])[lt] = ls.f;
-}
-
-template <int D, typename Act, typename Out>
-__device__ __forceinline__ void load_put_t(ChainLds<D, Act, Out> &L, const LoadSet<D, Act> &ls, int lt)
-{
-    using LS = LoadSet<D, Act>;
-    constexpr int TS = ChainLds<D, Act, Out>::TS;
-#pragma unroll
-    for (int i = 0; i < LS::TMP; ++i) {
-        const int idx = lt + kLoaders * i;
-        if (idx < LS::TMC) {
-            const int p = idx / 32, q = idx % 32;
-            *(u32x4 *)(L.t16 + (16 * tile_i(p) + chunk_row(q)) * TS + 16 * tile_j(p) + chunk_col(q)) =
-                ls.t[i];
-        }
+    for (int i = 0; i < SR::LP; ++i) {
+        const int idx = tid + 256 * i;
+        if (idx < SR::VC)
+            L.xvr[idx] = R.ld[i];
+        else if (idx < SR::NLD)
+            ((u32x4 *)L.fac[buf])[idx - SR::VC] = R.ld[i];
     }
 }
 
-// Loader side: write the o tile of sub-chunk `cl` (staged in LDS by the compute waves).
-template <int D, typename Act, typename Out>
-__device__ __forceinline__ void store_o(const ChainLds<D, Act, Out> &L, const ChainArgs &a, int lt,
-                                        int cl, Out *__restrict__ o)
+// One step of the chain over sub-chunk `cl` with register set K (step index modulo 3).
+template <int K, int D, typename Act, typename Out, bool SILU>
+__device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act> (&R)[3],
+                                           const ChainArgs &a, int cl, int nsub, f32x4 (&S)[D / 64],
+                                           float w0, float w1, float w2, float w3, float scale,
+                                           const Workspace &ws)
 {
-    constexpr int OEPC = 16 / (int)sizeof(Out);  // outputs per 16-byte chunk
-    constexpr int OCR = 16 / OEPC;               // chunks per row
-    const int rb = cl * kC, nv = min(kC, a.seg_n - rb);
-    if (lt < kC * OCR) {
-        const int row = lt / OCR, cc = (lt % OCR) * OEPC;
-        const u32x4 v = *(const u32x4 *)(L.obuf + row * 16 + cc);
-        if (row < nv) *(u32x4 *)(o + ((a.seg_row0 + rb + row) * a.Hv + a.h) * D + a.c0 + cc) = v;
-    }
-}
-
-// One loader step: K is the step index modulo 4 (static, so the register sets stay registers).
-template <int K, int D, typename Act, typename Out>
-__device__ __forceinline__ void loader_step(ChainLds<D, Act, Out> &L, LoadSet<D, Act> (&sets)[4],
-                                            const ChainArgs &a, int lt, int cl, int nsub,
-                                            const Act *__restrict__ x, const Act *win,
-                                            const Workspace &ws, Out *__restrict__ o)
-{
+    using CL = ChainLds<D, Act>;
+    using SR = StepRegs<D, Act>;
+    constexpr int HS = CL::HS, TS = CL::TS, ST = CL::ST;
+    constexpr int TPW = D / 64;  // d_k tiles per wave
     if (cl >= nsub) return;
-    const int nxt = (cl + 1) & 1;
-    if (cl + 3 < nsub) load_issue<D, Act>(sets[(K + 3) % 4], a, lt, cl + 3, x, win, ws);
-    if (cl > 0) store_o<D, Act, Out>(L, a, lt, cl - 1, o);
-    __syncthreads();  // #1
-    if (cl + 1 < nsub) load_put_early<D, Act, Out>(L, sets[(K + 1) % 4], lt, nxt);
-    __syncthreads();  // #2
-    if (cl + 1 < nsub) load_put_t<D, Act, Out>(L, sets[(K + 1) % 4], lt);
-    __syncthreads();  // #3
+    StepRegs<D, Act> &C = R[K];
+    const int wave = a.wave, col = a.col, kg = a.kg, lane = a.kg * 16 + a.col;
+    const int r0 = 16 * wave + 4 * kg;
+    const float *F = L.fac[cl & 1];
+    step_issue<D, Act>(R[(K + 2) % 3], a, min(cl + 2, nsub - 1), ws);
+
+    // X = K S and P = Q S for row tile `wave`
+    f32x4 X = {0.f, 0.f, 0.f, 0.f}, P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < SR::KB; ++kb) {
+        const half8 bS = *(const half8 *)(L.s16t + col * ST + 32 * kb + 8 * kg);
+        X = mfma16(C.kf[kb], bS, X);
+        P = mfma16(C.qf[kb], bS, P);
+    }
+    // R = beta V - beta gamma X; the state part of O is gamma P
+    f32x4 Ob;
+    {
+        const Act *vrows = (const Act *)L.xvr;
+        const f32x4 fb = *(const f32x4 *)(F + r0), fbg = *(const f32x4 *)(F + kC + r0);
+        const f32x4 fg = *(const f32x4 *)(F + 2 * kC + r0);
+        float vr[7];
+#pragma unroll
+        for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * 16 + col]);
+        half4 rv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v = w0 * vr[i] + w1 * vr[i + 1] + w2 * vr[i + 2] + w3 * vr[i + 3];
+            if constexpr (SILU) v = v / (1.f + expf(-v));
+            rv[i] = (_Float16)(fb[i] * v - fbg[i] * X[i]);
+            Ob[i] = fg[i] * P[i];
+        }
+        *(half4 *)(L.rt + col * TS + r0) = rv;
+    }
+    __syncthreads();  // #1: rt complete; xvr, K and the other factor buffer are free
+
+    // this step's K rows into LDS for the state update; next step's v rows and factors
+#pragma unroll
+    for (int kb = 0; kb < SR::KB; ++kb)
+        *(half8 *)(L.k16 + (16 * wave + col) * HS + 32 * kb + 8 * kg) = C.kf[kb];
+    put_ld<D, Act>(L, R[(K + 1) % 3], a.tid, (cl + 1) & 1);
+
+    // D = Tinv R (fragments above the diagonal are zero)
+    f32x4 Dl = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        Dl = mfma16(C.tf[kb], *(const half8 *)(L.rt + col * TS + 32 * kb + 8 * kg), Dl);
+    {
+        const f32x4 fd = *(const f32x4 *)(F + 3 * kC + r0);
+        half4 dv, ddv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            dv[i] = (_Float16)Dl[i];
+            ddv[i] = (_Float16)(fd[i] * Dl[i]);
+        }
+        *(half4 *)(L.dt + col * TS + r0) = dv;
+        *(half4 *)(L.ddt + col * TS + r0) = ddv;
+    }
+    __syncthreads();  // #2: dt, ddt and K complete
+
+    // S' = gamma_n S + K^T (exp(G_n - G) D)
+    {
+        const float gn = F[3 * kC - 1];
+        half8 bd[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) bd[kb] = *(const half8 *)(L.ddt + col * TS + 32 * kb + 8 * kg);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int kt = wave * TPW + t;
+            f32x4 acc = S[t] * gn;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                acc = mfma16(ktrans_frag(L.k16, HS, 32 * kb, 16 * kt, lane), bd[kb], acc);
+            S[t] = acc;
+            half4 sv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sv[i] = (_Float16)acc[i];
+            *(half4 *)(L.s16t + col * ST + 16 * kt + 4 * kg) = sv;
+        }
+    }
+    // O = scale (gamma Q S + M D)
+    {
+        f32x4 Oa = Ob;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            Oa = mfma16(C.mf[kb], *(const half8 *)(L.dt + col * TS + 32 * kb + 8 * kg), Oa);
+        const int obase = ((cl * kC + r0) * a.Hv + a.h) * D + a.c0 + col;  // element offset
+#pragma unroll
+        for (int i = 0; i < 4; ++i) store_out_buf<Out>(a.ro, obase + i * a.Hv * D, scale * Oa[i]);
+    }
+    __syncthreads();  // #3: s16t complete for the next step
 }
 
 // ------------------------------------------------------------------------------------------
 // chain_kernel: the serial walk of one (d_v tile, value head, sequence) over its sub-chunks.
-// Waves 0-3 compute; waves 4-11 load: they keep the inputs of the next three sub-chunks in
-// flight in registers, write the next sub-chunk's inputs into LDS between the step's barriers
-// and store each finished o tile, so the compute waves issue no global memory operation in
-// the loop.  Every step has three barriers on both sides.
+// Four waves; wave w owns rows 16w .. 16w+15 of every 64-row product and d_k rows
+// 32w .. 32w+31 (D = 128) of the state tile.  Each wave loads its own MFMA fragments straight
+// into registers two sub-chunks ahead; K (needed transposed by the other waves), the raw v rows
+// and the factor table pass through LDS.  Three barriers per step.
 // ------------------------------------------------------------------------------------------
-template <int D, typename Act, typename Out>
-__global__ __launch_bounds__(256 + kLoaders) void chain_kernel(SegArgs sa, const Act *__restrict__ x,
+template <int D, typename Act, typename Out, bool SILU>
+__global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__restrict__ x,
                                                     const Act *__restrict__ conv_w, int conv_on,
-                                                    int silu, int Hk, int Hv, float scale,
-                                                    Workspace ws, Out *__restrict__ o)
+                                                    int Hk, int Hv, float scale, Workspace ws,
+                                                    Out *__restrict__ o)
 {
-    using CL = ChainLds<D, Act, Out>;
-    constexpr int HS = CL::HS, TS = CL::TS, ST = CL::ST;
-    constexpr int NT = D / 16;      // d_k tiles of the state
-    constexpr int TPW = NT / 4;     // d_k tiles per compute wave
+    using CL = ChainLds<D, Act>;
+    using SR = StepRegs<D, Act>;
+    constexpr int ST = CL::ST;
+    constexpr int TPW = D / 64;
     __shared__ __attribute__((aligned(16))) CL L;
 
     // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  Units (value head,
@@ -581,50 +644,31 @@ __global__ __launch_bounds__(256 + kLoaders) void chain_kernel(SegArgs sa, const
     a.c0 = tile * 16;
     a.vch = 2 * Hk * D + h * D + a.c0;
     a.conv_on = conv_on;
+    a.tid = threadIdx.x;
+    a.wave = threadIdx.x >> 6;
+    a.col = threadIdx.x % 16;
+    a.kg = (threadIdx.x & 63) / 16;
     const Act *win = (const Act *)sa.seg[s].win_in;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int nsub = (a.seg_n + kC - 1) / kC;
-
-    if (wave >= 4) {
-        // ---------------------------------------------------------------- loader waves
-        const int lt = tid - 256;
-        for (int e = lt; e < kC * kC; e += kLoaders) {  // tiles above the diagonal: zero, never written
-            const int r = e / kC, c = e % kC;
-            if (c / 16 > r / 16) {
-                L.t16[r * TS + c] = (_Float16)0.f;
-                L.m16[0][r * TS + c] = (_Float16)0.f;
-                L.m16[1][r * TS + c] = (_Float16)0.f;
-            }
-        }
-        LoadSet<D, Act> sets[4];
-        if (nsub > 0) load_issue<D, Act>(sets[0], a, lt, 0, x, win, ws);
-        if (nsub > 1) load_issue<D, Act>(sets[1], a, lt, 1, x, win, ws);
-        if (nsub > 2) load_issue<D, Act>(sets[2], a, lt, 2, x, win, ws);
-        if (nsub > 0) {
-            load_put_early<D, Act, Out>(L, sets[0], lt, 0);
-            load_put_t<D, Act, Out>(L, sets[0], lt);
-        }
-        __syncthreads();  // #0
-        for (int cl = 0; cl < nsub; cl += 4) {
-            loader_step<0>(L, sets, a, lt, cl, nsub, x, win, ws, o);
-            loader_step<1>(L, sets, a, lt, cl + 1, nsub, x, win, ws, o);
-            loader_step<2>(L, sets, a, lt, cl + 2, nsub, x, win, ws, o);
-            loader_step<3>(L, sets, a, lt, cl + 3, nsub, x, win, ws, o);
-        }
-        if (nsub > 0) store_o<D, Act, Out>(L, a, lt, nsub - 1, o);
-        return;
-    }
-
-    // -------------------------------------------------------------------- compute waves
-    const int col = lane % 16, kg = lane / 16;
     const float *S_in = sa.seg[s].S_in;
     float *S_out = sa.seg[s].S_out;
+    const int nsub = (a.seg_n + kC - 1) / kC;
+    const int wave = a.wave, col = a.col, kg = a.kg;
+    a.rx = __builtin_amdgcn_make_buffer_rsrc((void *)(x + a.seg_row0 * a.C), 0,
+                                             a.seg_n * a.C * (int)sizeof(Act), kRsrcWord3);
+    a.ro = __builtin_amdgcn_make_buffer_rsrc((void *)(o + a.seg_row0 * Hv * D), 0,
+                                             a.seg_n * Hv * D * (int)sizeof(Out), kRsrcWord3);
+
     float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f;
     if (conv_on) {
         w0 = to_f32(conv_w[(a.vch + col) * 4 + 0]);
         w1 = to_f32(conv_w[(a.vch + col) * 4 + 1]);
         w2 = to_f32(conv_w[(a.vch + col) * 4 + 2]);
         w3 = to_f32(conv_w[(a.vch + col) * 4 + 3]);
+    }
+    StepRegs<D, Act> R[3];
+    if (nsub > 0) {
+        step_issue<D, Act>(R[0], a, 0, ws);
+        step_issue<D, Act>(R[1], a, min(1, nsub - 1), ws);
     }
     f32x4 S[TPW];
 #pragma unroll
@@ -639,97 +683,19 @@ __global__ __launch_bounds__(256 + kLoaders) void chain_kernel(SegArgs sa, const
         }
         *(half4 *)(L.s16t + col * ST + 16 * kt + 4 * kg) = sv;
     }
-    __syncthreads();  // #0
-    const Act *vrows = (const Act *)L.xvr;  // raw v of (halo ++ rows), 16 columns per row
-    const int r0 = 16 * wave + 4 * kg;      // this lane's first row in the sub-chunk
-
-    for (int cl = 0; cl < nsub; ++cl) {
-        const int cur = cl & 1;
-        const float *F = L.fac[cur];
-
-        // X = K S and P = Q S for row tile `wave`
-        f32x4 X = {0.f, 0.f, 0.f, 0.f}, P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < D / 32; ++kb) {
-            const int off = 32 * kb + 8 * kg;
-            const half8 bS = *(const half8 *)(L.s16t + col * ST + off);
-            X = mfma16(*(const half8 *)(L.k16[cur] + (16 * wave + col) * HS + off), bS, X);
-            P = mfma16(*(const half8 *)(L.q16 + (16 * wave + col) * HS + off), bS, P);
-        }
-        // R = beta V - beta gamma X; the state part of O is gamma P
-        f32x4 Ob;
-        {
-            float vr[7];
-#pragma unroll
-            for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * 16 + col]);
-            half4 rv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = r0 + i;
-                float v = w0 * vr[i] + w1 * vr[i + 1] + w2 * vr[i + 2] + w3 * vr[i + 3];
-                if (silu && conv_on) v = v / (1.f + expf(-v));
-                rv[i] = (_Float16)(F[r] * v - F[kC + r] * X[i]);
-                Ob[i] = F[2 * kC + r] * P[i];
-            }
-            *(half4 *)(L.rt + col * TS + r0) = rv;
-        }
-        __syncthreads();  // #1
-
-        // D = Tinv R (tiles above the diagonal of Tinv are zero)
-        f32x4 Dl = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int off = 32 * kb + 8 * kg;
-            Dl = mfma16(*(const half8 *)(L.t16 + (16 * wave + col) * TS + off),
-                        *(const half8 *)(L.rt + col * TS + off), Dl);
-        }
-        {
-            half4 dv, ddv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                dv[i] = (_Float16)Dl[i];
-                ddv[i] = (_Float16)(F[3 * kC + r0 + i] * Dl[i]);
-            }
-            *(half4 *)(L.dt + col * TS + r0) = dv;
-            *(half4 *)(L.ddt + col * TS + r0) = ddv;
-        }
-        __syncthreads();  // #2
-
-        // S' = gamma_n S + K^T (exp(G_n - G) D)
-        {
-            const float gn = F[2 * kC + kC - 1];
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                const int kt = wave * TPW + t;
-                f32x4 acc = S[t] * gn;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int off = 32 * kb + 8 * kg;
-                    acc = mfma16(ktrans_frag(L.k16[cur], HS, 32 * kb, 16 * kt, lane),
-                                 *(const half8 *)(L.ddt + col * TS + off), acc);
-                }
-                S[t] = acc;
-                half4 sv;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sv[i] = (_Float16)acc[i];
-                *(half4 *)(L.s16t + col * ST + 16 * kt + 4 * kg) = sv;
-            }
-        }
-        // O = scale (gamma Q S + M D), staged in LDS for the loader waves
-        {
-            f32x4 Oa = Ob;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int off = 32 * kb + 8 * kg;
-                Oa = mfma16(*(const half8 *)(L.m16[cur] + (16 * wave + col) * TS + off),
-                            *(const half8 *)(L.dt + col * TS + off), Oa);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) store_out(L.obuf + (r0 + i) * 16 + col, scale * Oa[i]);
-        }
-        __syncthreads();  // #3
+    if (nsub > 0) put_ld<D, Act>(L, R[0], a.tid, 0);
+    __syncthreads();
+    // the 3 halo rows of the first sub-chunk come from the window (the x loads gave 0 there)
+    if (conv_on && nsub > 0 && a.tid < 3 * SR::VCR) {
+        const int vr = a.tid / SR::VCR, cc = (a.tid % SR::VCR) * SR::EPC;
+        L.xvr[a.tid] = L.xvr[a.tid] | *(const u32x4 *)(win + (int64_t)vr * a.C + a.vch + cc);
     }
-
+    __syncthreads();
+    for (int cl = 0; cl < nsub; cl += 3) {
+        chain_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, S, w0, w1, w2, w3, scale, ws);
+        chain_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, S, w0, w1, w2, w3, scale, ws);
+        chain_step<2, D, Act, Out, SILU>(L, R, a, cl + 2, nsub, S, w0, w1, w2, w3, scale, ws);
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int kt = wave * TPW + t;
@@ -829,14 +795,24 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
     const int conv_on = d.conv_width > 0 ? 1 : 0;
     const int C = 2 * d.n_k_heads * D + d.n_v_heads * D;
     em.mark(0);
-    hipLaunchKernelGGL((prep_kernel<D, Act>), dim3(sa.n_sub, d.n_k_heads), dim3(256), 0, st, sa,
-                       (const Act *)x, (const Act *)conv_w, conv_on, d.conv_silu, g, beta,
-                       d.n_k_heads, d.n_v_heads, d.l2_eps, ws);
+    if (d.conv_silu && conv_on)
+        hipLaunchKernelGGL((prep_kernel<D, Act, true>), dim3(sa.n_sub, d.n_k_heads), dim3(256), 0, st,
+                           sa, (const Act *)x, (const Act *)conv_w, conv_on, g, beta, d.n_k_heads,
+                           d.n_v_heads, d.l2_eps, ws);
+    else
+        hipLaunchKernelGGL((prep_kernel<D, Act, false>), dim3(sa.n_sub, d.n_k_heads), dim3(256), 0, st,
+                           sa, (const Act *)x, (const Act *)conv_w, conv_on, g, beta, d.n_k_heads,
+                           d.n_v_heads, d.l2_eps, ws);
     em.mark(1);
     em.mark(2);
-    hipLaunchKernelGGL((chain_kernel<D, Act, Out>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
-                       dim3(256 + kLoaders), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
-                       d.conv_silu, d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
+    if (d.conv_silu && conv_on)
+        hipLaunchKernelGGL((chain_kernel<D, Act, Out, true>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
+                           dim3(256), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
+                           d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
+    else
+        hipLaunchKernelGGL((chain_kernel<D, Act, Out, false>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
+                           dim3(256), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
+                           d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
     em.mark(3);
     em.mark(4);
     if (conv_on)
