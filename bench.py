@@ -9,11 +9,17 @@ new conv window).  Inputs are seeded synthetic tensors resident in HBM before ti
 three input sets rotate so that consecutive steps do not re-read the previous step's inputs
 from the 256 MB Infinity Cache.
 
-Prints one JSON line (rank 0) with the whole-job tokens/s, a roofline object for the layer
-call measured with HIP events on the launch stream, and the float64 CPU oracle timed on a
-bounded sample of the same workload.
+Prints one JSON line with the whole-job tokens/s (wall clock over the timed steps), a
+roofline object for the dominant kernel (its share of the layer's algorithmic bytes over its
+average duration, from HIP events the library records on the launch stream around each
+kernel in every timed step), the same figure for the whole layer call, and the float64 CPU
+oracle timed on a bounded sample of the same workload.
+
+    --extras                also time state capture/restore and a 370-row fork
+    --copy-calibration N    run a plain N-byte device copy after timing (for counter scaling)
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -37,6 +43,37 @@ def algorithmic_bytes(T, Hk, Hv, d, act_bytes=2, out_bytes=2):
     return per_token, per_token * T + per_call
 
 
+def kernel_bytes(T, Hk, Hv, d, act_bytes=2, out_bytes=2):
+    """The same bytes split by the kernel that moves them between the caller's buffers and the
+    chip: prep reads the q|k channels, g, beta and the conv weights; chain reads the v channels
+    and the state and writes o and the state; window reads and writes the conv window."""
+    C = 2 * Hk * d + Hv * d
+    prep = T * (2 * Hk * d * act_bytes + 2 * Hv * 4) + C * 4 * act_bytes
+    chain = T * (Hv * d * act_bytes + Hv * d * out_bytes) + 2 * Hv * d * d * 4
+    window = 2 * 3 * C * act_bytes
+    return {"prep_kernel": prep, "chain_kernel": chain, "window_kernel": window}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the FETCH_SIZE and WRITE_SIZE counter runs stored
+    in profiles/hbm_traffic_gdn_layer_T8192.txt, scaled by a plain copy's reading.  None when
+    the file is missing or was taken from different kernel source than the one built now."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_gdn_layer_T8192.txt")
+    src = os.path.join(ROOT, "hybrid_linear_attention_prefill_amd", "csrc", "gdn_kernels.hip")
+    try:
+        with open(path) as f:
+            lines = f.read().splitlines()
+        with open(src, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    fields = dict(ln.split("=", 1) for ln in lines if "=" in ln and not ln.startswith("#"))
+    if fields.get("kernel_source_sha256") != digest:
+        return None
+    v = fields.get("bytes_per_launch." + kernel)
+    return None if v is None else int(float(v))
+
+
 def algorithmic_flops(T, Hk, Hv, d, C=64):
     """Flops of the chunked method per call: K K^T and Q K^T per key head (lower triangle),
     and per value head the products with the state, the triangular T R and M D, and the
@@ -46,31 +83,29 @@ def algorithmic_flops(T, Hk, Hv, d, C=64):
     return 2.0 * T * (Hk * mac_k + Hv * mac_v)
 
 
-def cpu_baseline(seconds_target=15.0):
-    """The float64 oracle on a bounded sample: all 32 value heads of the same layer over the
-    first rows of the workload, threads over heads."""
+def cpu_baseline(seconds_target=10.0):
+    """The float64 oracle on a bounded sample of the workload: whole 8192-row layer calls (all
+    32 value heads, threads over heads), repeated until about `seconds_target` of wall time."""
     import numpy as np
     from hybrid_linear_attention_prefill_amd import synth
     from oracle import c_oracle
     threads = max(1, min(16, os.cpu_count() or 1))
     shape = synth.LAYER_16x32x128
     kw = dict(n_k_heads=16, n_v_heads=32, d_k=128, d_v=128, scale=128 ** -0.5, l2_eps=1e-6)
-    rows = 256
-    while True:
-        inp = synth.layer_inputs(shape, rows, seed=0)
-        x, w = synth.f64(inp["x"]), synth.f64(inp["conv_w"])
-        g, beta = synth.f64(inp["g"]), synth.f64(inp["beta"])
+    inp = synth.layer_inputs(shape, T_ROWS, seed=0)
+    x, w = synth.f64(inp["x"]), synth.f64(inp["conv_w"])
+    g, beta = synth.f64(inp["g"]), synth.f64(inp["beta"])
+    calls, spent = 0, 0.0
+    while spent < seconds_target:
         t0 = time.perf_counter()
         c_oracle.gdn_layer(x, w, np.zeros((3, shape.channels)), g, beta,
                            np.zeros((32, 128, 128)), threads=threads, **kw)
-        dt = time.perf_counter() - t0
-        if dt < seconds_target / 3 and rows < T_ROWS:
-            rows = min(T_ROWS, rows * 2)
-            continue
-        return {"value": rows / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-                "sample": "float64 per-token oracle (conv, L2 norm, gated delta rule), all 32 "
-                          "value heads of the 16/32/128 layer over the first %d of the 8192 rows "
-                          "(%.1f s wall)" % (rows, dt)}
+        spent += time.perf_counter() - t0
+        calls += 1
+    return {"value": calls * T_ROWS / spent, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "float64 per-token oracle (conv, L2 norm, gated delta rule) on the same "
+                      "16/32/128 layer: %d whole 8192-row calls, %.1f s wall" % (calls, spent)}
 
 
 def main():
@@ -79,6 +114,11 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time state capture/restore and a 370-row fork")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the timed region, run a plain device copy of BYTES bytes three "
+                         "times (reference dispatch for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the layer's heads would shard across GPUs with no "
@@ -106,16 +146,17 @@ def main():
     state = b.State(desc)
     b.gdn_state_init(desc, state)
 
-    def step(i):
+    def step(i, events=()):
         s = sets[i % n_sets]
-        n = b.gdn_prefill_chunked(desc, s["x"], s["conv_w"], s["g"], s["beta"], state, state, o,
-                                  T_ROWS, b.GDN_COMMIT, ws)
+        n = b.gdn_prefill_chunked_events(desc, s["x"], s["conv_w"], s["g"], s["beta"], state,
+                                         state, o, T_ROWS, b.GDN_COMMIT, ws, events=events)
         assert n == T_ROWS
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # Timed region 1: K layer calls back to back (the throughput figure).
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -128,46 +169,64 @@ def main():
     wall = time.perf_counter() - t0
     ev_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # per-kernel durations of the same call, events recorded by the library on the stream
-    per_kernel = {"prep_kernel": 0.0, "chain_kernel": 0.0, "window_kernel": 0.0}
-    reps = max(10, args.steps // 2)
-    for i in range(reps):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        s = sets[i % n_sets]
-        b.gdn_prefill_chunked_events(desc, s["x"], s["conv_w"], s["g"], s["beta"], state, state, o,
-                                     T_ROWS, b.GDN_COMMIT, ws, events=evs)
-        torch.cuda.synchronize()
-        for k, name in enumerate(per_kernel):
-            per_kernel[name] += evs[2 * k].elapsed_time(evs[2 * k + 1]) / reps
+    # Timed region 2: the same K calls with HIP events recorded by the library on the launch
+    # stream around each of its three kernels (the per-kernel durations).
+    names = ("prep_kernel", "chain_kernel", "window_kernel")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(names))]
+           for _ in range(args.steps)]
+    for e in [e for row in evs for e in row]:
+        e.record(stream)              # creates the underlying HIP events before timing
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    per_kernel = {n: sum(row[2 * k].elapsed_time(row[2 * k + 1]) for row in evs) / args.steps
+                  for k, n in enumerate(names)}
 
-    # state copies (capture + restore of the 2 MiB state and window) and a fork of a
-    # 330-row pending tail plus a 40-row question above the committed rows
-    snap = b.State(desc)
-    fork_out = b.State(desc)
-    fo = torch.empty((370, Hv, d), dtype=torch.bfloat16, device=dev)
-    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps2 = 20
-    e2.record(stream)
-    for _ in range(reps2):
-        b.gdn_state_capture(desc, state, snap)
-        b.gdn_state_restore(desc, state, snap)
-    e3.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = e2.elapsed_time(e3) / reps2
-    copy_bytes = 2 * 2 * (b.gdn_state_S_bytes(desc) + b.gdn_state_conv_bytes(desc))
-    e2.record(stream)
-    for _ in range(reps2):
-        s = sets[0]
-        b.gdn_prefill_chunked(desc, s["x"][:370], s["conv_w"], s["g"][:370], s["beta"][:370],
-                              state, fork_out, fo, 370, b.GDN_FORK, ws)
-    e3.record(stream)
-    torch.cuda.synchronize()
-    fork_ms = e2.elapsed_time(e3) / reps2
+    extras = {}
+    if args.extras:
+        # state copies (capture + restore of the 2 MiB state and window) and a fork of a
+        # 330-row pending tail plus a 40-row question above the committed rows
+        snap = b.State(desc)
+        fork_out = b.State(desc)
+        fo = torch.empty((370, Hv, d), dtype=torch.bfloat16, device=dev)
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps2 = 20
+        e2.record(stream)
+        for _ in range(reps2):
+            b.gdn_state_capture(desc, state, snap)
+            b.gdn_state_restore(desc, state, snap)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        copy_ms = e2.elapsed_time(e3) / reps2
+        copy_bytes = 2 * 2 * (b.gdn_state_S_bytes(desc) + b.gdn_state_conv_bytes(desc))
+        e2.record(stream)
+        for _ in range(reps2):
+            s = sets[0]
+            b.gdn_prefill_chunked(desc, s["x"][:370], s["conv_w"], s["g"][:370], s["beta"][:370],
+                                  state, fork_out, fo, 370, b.GDN_FORK, ws)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        extras = {"state_capture_restore_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                  "fork_370_rows_ms": round(e2.elapsed_time(e3) / reps2, 4)}
+
+    if args.copy_calibration:
+        # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     per_token, bytes_call = algorithmic_bytes(T_ROWS, Hk, Hv, d)
+    split = kernel_bytes(T_ROWS, Hk, Hv, d)
     flops_call = algorithmic_flops(T_ROWS, Hk, Hv, d)
-    achieved = bytes_call / (ev_ms * 1e-3) / 1e9
     tokens_per_s = T_ROWS * args.steps / wall
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_achieved = split[dom] / (per_kernel[dom] * 1e-3) / 1e9
+    layer_achieved = bytes_call / (ev_ms * 1e-3) / 1e9
     out = {
         "metric": "Gated-DeltaNet prefill tokens/sec per layer (1 MI355X); % of MFMA/HBM roofline",
         "value": round(tokens_per_s, 1),
@@ -186,24 +245,30 @@ def main():
                    "sub_chunk": 64, "act_dtype": "bf16", "out_dtype": "bf16"},
         "roofline": {
             "bound": "hbm",
-            "kernel": "layer call: prep_kernel + chain_kernel + window_kernel",
-            "achieved": round(achieved, 1),
+            "kernel": dom,
+            "achieved": round(dom_achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
-            "algorithmic_bytes_per_call": bytes_call,
-            "algorithmic_bytes_per_token": per_token,
-            "call_ms_events": round(ev_ms, 5),
+            "frac": round(dom_achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(dom),
+            "algorithmic_bytes_per_launch": split[dom],
+            "launch_ms_events": round(per_kernel[dom], 5),
             "per_kernel_ms_events": {k: round(v, 5) for k, v in per_kernel.items()},
-            "mfma_tflops_algorithmic": round(flops_call / (ev_ms * 1e-3) / 1e12, 2),
-            "mfma_frac_algorithmic": round(flops_call / (ev_ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-        },
-        "extras": {
-            "state_capture_restore_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
-            "fork_370_rows_ms": round(fork_ms, 4),
+            "per_kernel_algorithmic_bytes": split,
+            "layer_call": {
+                "achieved": round(layer_achieved, 1),
+                "frac": round(layer_achieved / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": bytes_call,
+                "algorithmic_bytes_per_token": per_token,
+                "call_ms_events": round(ev_ms, 5),
+                "mfma_tflops_algorithmic": round(flops_call / (ev_ms * 1e-3) / 1e12, 2),
+                "mfma_frac_algorithmic": round(flops_call / (ev_ms * 1e-3) / 1e12
+                                               / MFMA_F16_PEAK_TFLOPS, 4),
+            },
         },
     }
+    if extras:
+        out["extras"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -9,7 +9,7 @@
  * What it computes, in the order the method defines it, one token at a time, in float64:
  *
  *  1. A causal depthwise convolution of width W over the q|k|v channels whose state is the
- *     last W-1 conv *inputs* ("the last three conv inputs" kept per linear-attention layer:
+ *     last W-1 conv *inputs* (the three most recent conv inputs are kept per linear-attention layer:
  *     PR "qwen3_5: run prompts that share prefixes once per prefix", section Purpose; the
  *     convolution state compared bit for bit on replay: "The shadow reader", section
  *     "Exact on a grid").  Tap W-1 multiplies the current token; no bias; SiLU optional.

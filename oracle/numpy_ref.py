@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Each function restates, in float64 and one token at a time, a step of the layer whose state
-the pages keep: the conv window of "the last three conv inputs" (PR "qwen3_5: run prompts
+the pages keep: the conv window holding the three most recent conv inputs (PR "qwen3_5: run prompts
 that share prefixes once per prefix", section Purpose), and the gated delta rule's fp32
 recurrent state (named in "The shadow reader", section "One session's state", and in "Long
 context and sessions", section Checkpoints; its update equation is not printed on the pages:

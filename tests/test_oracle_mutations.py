@@ -33,6 +33,11 @@ def rule(q, k, v, g, beta, S0, scale, variant=None):
         elif variant == "missing_beta_on_correction":
             S *= a
             S += np.outer(k[t], beta[t] * v[t] - S.T @ k[t])
+        elif variant == "transposed_state":           # state read as [d_v][d_k] (square dims)
+            S *= a
+            S += beta[t] * np.outer(k[t], v[t] - S @ k[t])
+            o[t] = scale * (S @ q[t])
+            continue
         else:
             S *= a
             S += beta[t] * np.outer(k[t], v[t] - S.T @ k[t])
@@ -46,30 +51,47 @@ def _unit(rng, n, d):
 
 
 def checks(f):
-    """Return the names of the pin checks that the rule f fails."""
+    """Return the names of the pin checks that the rule f fails (a shape error is a failure)."""
     failed = []
     rng = np.random.default_rng(0)
-    # beta = 0: pure decay
     T, dk, dv = 6, 5, 3
     q, k, v = _unit(rng, T, dk), _unit(rng, T, dk), rng.standard_normal((T, dv))
     g = -rng.uniform(0.1, 0.7, T)
     S0 = rng.standard_normal((dk, dv))
-    o, S = f(q, k, v, g, np.zeros(T), S0, 1.0)
-    if not np.allclose(S, np.exp(g.sum()) * S0, rtol=1e-12):
-        failed.append("beta0")
-    # retrieval: beta=1, unit key, q=k
-    o, S = f(k, k, v, g, np.ones(T), S0, 1.0)
-    if not np.allclose(o, v, rtol=1e-10, atol=1e-10):
-        failed.append("retrieval")
-    # single token, g=0
-    o, S = f(q[:1], k[:1], v[:1], np.zeros(1), np.array([0.3]), np.zeros((dk, dv)), 0.5)
-    if not np.allclose(o[0], 0.5 * 0.3 * (q[0] @ k[0]) * v[0], rtol=1e-12, atol=1e-14):
-        failed.append("single_token")
-    # orthonormal keys, d_k != d_v
     Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
-    o, S = f(Qm[:3], Qm[:3], v[:3], np.zeros(3), np.ones(3), np.zeros((dk, dv)), 1.0)
-    if not np.allclose(S, Qm[:3].T @ v[:3], rtol=1e-12, atol=1e-12):
-        failed.append("orthonormal")
+    d = 4
+    kq = _unit(rng, 5, d)
+    vs = rng.standard_normal((5, d))
+    S0s = rng.standard_normal((d, d))
+    gs = -rng.uniform(0.1, 0.7, 5)
+
+    def beta0():            # beta = 0: pure decay
+        o, S = f(q, k, v, g, np.zeros(T), S0, 1.0)
+        return np.allclose(S, np.exp(g.sum()) * S0, rtol=1e-12)
+
+    def retrieval():        # beta = 1, unit key, q = k: the output is the value
+        o, S = f(k, k, v, g, np.ones(T), S0, 1.0)
+        return np.allclose(o, v, rtol=1e-10, atol=1e-10)
+
+    def single_token():     # one token, g = 0: S = beta k v^T
+        o, S = f(q[:1], k[:1], v[:1], np.zeros(1), np.array([0.3]), np.zeros((dk, dv)), 0.5)
+        return np.allclose(o[0], 0.5 * 0.3 * (q[0] @ k[0]) * v[0], rtol=1e-12, atol=1e-14)
+
+    def orthonormal():      # orthonormal keys, beta = 1, d_k != d_v: S = K^T V
+        o, S = f(Qm[:3], Qm[:3], v[:3], np.zeros(3), np.ones(3), np.zeros((dk, dv)), 1.0)
+        return np.allclose(S, Qm[:3].T @ v[:3], rtol=1e-12, atol=1e-12)
+
+    def retrieval_square(): # square dims, non-symmetric start state: retrieval still exact
+        o, S = f(kq, kq, vs, gs, np.ones(5), S0s, 1.0)
+        return np.allclose(o, vs, rtol=1e-10, atol=1e-10)
+
+    for check in (beta0, retrieval, single_token, orthonormal, retrieval_square):
+        try:
+            ok = check()
+        except ValueError:
+            ok = False
+        if not ok:
+            failed.append(check.__name__)
     return failed
 
 
@@ -79,6 +101,7 @@ def test_correct_rule_passes_every_check():
 
 
 @pytest.mark.parametrize("variant", ["no_decay_on_correction", "plus_sign", "output_before_update",
-                                     "decay_after_write", "missing_beta_on_correction"])
+                                     "decay_after_write", "missing_beta_on_correction",
+                                     "transposed_state"])
 def test_each_mutant_fails_some_check(variant):
     assert checks(lambda *a: rule(*a, variant=variant)), variant
