@@ -15,7 +15,9 @@ constexpr int kC = GDN_SUB_CHUNK;  // 64 rows per sub-chunk
 constexpr int kTileV = 16;         // d_v columns of the state owned by one chain workgroup
 // A lower-triangular 64x64 factor (Tinv or M) is stored as the MFMA A fragments that the chain
 // kernel's waves load: (row tile w, 32-wide K step kb) for (0,0) (1,0) (2,0) (2,1) (3,0) (3,1),
-// each 64 lanes x 8 fp16 (lane l: row 16w + l%16, columns 32kb + 8(l/16) .. +7).
+// each 64 lanes x 8 fp16.  Lane l holds row 16w + l%16; its element e is column
+// 32kb + 16(e/4) + 4(l/16) + e%4 (the K order of the step is permuted; the chain kernel
+// stores the matching B operand rows in the same order).
 constexpr int kTriFrags = 6;
 constexpr int kPackedTri = kTriFrags * 64 * 8;
 
@@ -43,8 +45,8 @@ struct Workspace {
     _Float16 *Qh;  // [n_sub][Hk][64*d]  normalised q, fp16, in MFMA A-fragment order
     _Float16 *Kh;  // [n_sub][Hk][64*d]  normalised k, likewise: fragment (w, kb) lane l holds
                    //                    row 16w + l%16, columns 32kb + 8(l/16) .. +7
-    _Float16 *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1 fragments, fp16
-    _Float16 *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay fragments, fp16
+    _Float16 *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1 fragments, fp16 (order above)
+    _Float16 *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay fragments, fp16 (order above)
     float *Fac;    // [n_sub][Hv][4][64]  per row: beta, beta*gamma, gamma, exp(G_n - G) (fp32)
 };
 

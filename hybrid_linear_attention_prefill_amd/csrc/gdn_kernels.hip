@@ -157,17 +157,20 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
     constexpr int XSC = CPR + 1;                // LDS row stride of raw x, in chunks
     constexpr int HS = D + 8;                   // fp16 row stride of q, k
     constexpr int AS = kC + 4;                  // fp32 row stride of A, Tinv
-    constexpr int RS = 16 + 4;                  // fp32 row stride of a 16x16 staging tile
     constexpr int XBYTES = XR * XSC * 16;
-    constexpr int ABYTES = 2 * kC * AS * 4;
-    __shared__ __attribute__((aligned(16))) unsigned char ubuf[XBYTES > ABYTES ? XBYTES : ABYTES];
-    __shared__ __attribute__((aligned(16))) _Float16 q16[kC * HS];
-    __shared__ __attribute__((aligned(16))) _Float16 k16[kC * HS];
-    __shared__ __attribute__((aligned(16))) float Rs[4][16 * RS];
-    __shared__ float Gs[kC], bs[kC];
-    u32x4 *const xs = (u32x4 *)ubuf;       // phases 1-2: raw x rows
-    float *const As = (float *)ubuf;       // phase 4: A and Tinv
-    float *const Ts = As + kC * AS;
+    constexpr int QBYTES = kC * HS * 2;
+    constexpr int TBYTES = kC * AS * 4;         // one 64 x 64 fp32 factor
+    constexpr int P13 = XBYTES + 2 * QBYTES;
+    constexpr int UBYTES = P13 > 4 * TBYTES ? P13 : 4 * TBYTES;
+    // Phases 1-3 use raw x rows, q16 and k16; phase 4 reuses the same bytes for A and Tinv of
+    // two value heads.
+    __shared__ __attribute__((aligned(16))) unsigned char ubuf[UBYTES];
+    __shared__ __attribute__((aligned(16))) float Gs[2][kC], bs[2][kC];
+    u32x4 *const xs = (u32x4 *)ubuf;
+    _Float16 *const q16 = (_Float16 *)(ubuf + XBYTES);
+    _Float16 *const k16 = q16 + kC * HS;
+#define AS_OF(hh) ((float *)(ubuf + (hh) * TBYTES))
+#define TS_OF(hh) ((float *)(ubuf + (2 + (hh)) * TBYTES))
 
     const int sub = blockIdx.x, kh = blockIdx.y;
     const int s = find_seg(sa, sub);
@@ -270,7 +273,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
         }
     }
 
-    // 3. K K^T and Q K^T, row tile `wave`, column tiles j <= wave
+    // 3. K K^T and Q K^T for row tile `wave`, column tiles j <= wave, with the operands swapped
+    //    so that lane (g = lane / 16, cc = lane % 16) holds, for column tile j, the entries
+    //    [16 wave + cc][16 j + 4 g + i], i = 0..3: one row per lane, four adjacent columns.
     f32x4 kk[4], qk[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -280,21 +285,23 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
 #pragma unroll
             for (int kb = 0; kb < D / 32; ++kb) {
                 const int off = 32 * kb + 8 * (lane / 16);
-                const half8 ka = *(const half8 *)(k16 + (16 * wave + lane % 16) * HS + off);
-                const half8 qa = *(const half8 *)(q16 + (16 * wave + lane % 16) * HS + off);
-                const half8 kbv = *(const half8 *)(k16 + (16 * j + lane % 16) * HS + off);
-                kk[j] = mfma16(ka, kbv, kk[j]);
-                qk[j] = mfma16(qa, kbv, qk[j]);
+                const half8 kw = *(const half8 *)(k16 + (16 * wave + lane % 16) * HS + off);
+                const half8 qw = *(const half8 *)(q16 + (16 * wave + lane % 16) * HS + off);
+                const half8 kj = *(const half8 *)(k16 + (16 * j + lane % 16) * HS + off);
+                kk[j] = mfma16(kj, kw, kk[j]);
+                qk[j] = mfma16(kj, qw, qk[j]);
             }
         }
     }
 
-    // 4. per value head of this key head's group
+    // 4. the value heads of this key head's group, two at a time (head pair slot hh = 0, 1)
     const int group = Hv / Hk;
-    for (int hh = 0; hh < group; ++hh) {
-        const int h = kh * group + hh;
-        if (wave == 0) {  // cumulative log decay (inclusive scan) and beta; 0 past the end
-            const int r = lane;
+    const int g4 = lane / 16, cc = lane % 16;
+    const int row = 16 * wave + cc;  // this lane's row of the Gram tiles
+    for (int hp = 0; hp < group; hp += 2) {
+        const int nh = min(2, group - hp);
+        if (wave < nh) {  // cumulative log decay (inclusive scan) and beta; 0 past the end
+            const int h = kh * group + hp + wave, r = lane;
             float gv = (r < nv) ? g[(seg_row0 + r_base + r) * Hv + h] : 0.f;
             const float bv = (r < nv) ? beta[(seg_row0 + r_base + r) * Hv + h] : 0.f;
 #pragma unroll
@@ -302,8 +309,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
                 const float t = __shfl_up(gv, off);
                 if (lane >= off) gv += t;
             }
-            Gs[r] = gv;
-            bs[r] = bv;
+            Gs[wave][r] = gv;
+            bs[wave][r] = bv;
             const float Gn = __shfl(gv, 63);
             const float gam = expf(gv);
             float *F = ws.Fac + ((int64_t)sub * Hv + h) * 4 * kC;
@@ -312,100 +319,149 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             F[2 * kC + r] = gam;
             F[3 * kC + r] = expf(Gn - gv);
         }
-        __syncthreads();
+        __syncthreads();  // gates ready; raw rows, q16 and k16 are no longer read
 
-        // A into LDS (fp32, zeros on and above the diagonal); M stays in registers for now
-        f32x4 mreg[4];
-        {
+        // A = strict_lower(beta K K^T * decay) into LDS (fp32); M = lower(Q K^T * decay) from
+        // registers to the workspace.  Fragment (w, kb) of M, lane l, element e holds column
+        // 32 kb + 16 (e / 4) + 4 (l / 16) + e % 4 of row 16 w + l % 16, which is this lane's
+        // tile 2 kb + e / 4, entry e % 4.
+        for (int hh = 0; hh < nh; ++hh) {
+            const int h = kh * group + hp + hh;
+            const float Gr = Gs[hh][row], br = bs[hh][row];
+            f32x4 mt[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
+                mt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (j <= wave) {
+                    const f32x4 Gc = *(const f32x4 *)(&Gs[hh][16 * j + 4 * g4]);
+                    f32x4 at;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * wave + 4 * (lane / 16) + i, c = 16 * j + lane % 16;
-                    float a = 0.f, m = 0.f;
-                    if (j <= wave && c <= r) {
-                        const float dec = expf(Gs[r] - Gs[c]);
-                        m = qk[j][i] * dec;
-                        if (c < r) a = bs[r] * kk[j][i] * dec;
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = 16 * j + 4 * g4 + i;
+                        const float dec = (c <= row) ? expf(Gr - Gc[i]) : 0.f;
+                        mt[j][i] = qk[j][i] * dec;
+                        at[i] = (c < row) ? br * kk[j][i] * dec : 0.f;
                     }
-                    As[r * AS + c] = a;
-                    mreg[j][i] = m;
+                    *(f32x4 *)(AS_OF(hh) + row * AS + 16 * j + 4 * g4) = at;
+                }
+            }
+            _Float16 *Mg = ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                if (kb == 0 || wave >= 2) {
+                    half8 hv;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hv[e] = (_Float16)mt[2 * kb + e / 4][e % 4];
+                    *(half8 *)(Mg + (tri_frag(wave, kb) * 64 + lane) * 8) = hv;
                 }
             }
         }
-        __syncthreads();
+        __syncthreads();  // A complete
 
-        // Tinv = (I + A)^-1.  Phase 1: the four diagonal 16x16 blocks by forward substitution,
-        // lane = 16 b + column (wave 0).  The other blocks of Ts are cleared meanwhile.
-        if (wave == 0) {
+        // Tinv = (I + A)^-1 by 16 x 16 blocks.  Diagonal blocks by forward substitution
+        // (wave hh, lane = 16 b + column); the upper blocks that the fragments cover,
+        // (0,1) and (2,3), are cleared by waves 2 and 3.
+        if (wave < nh) {
+            const float *Ah = AS_OF(wave);
+            float *Th = TS_OF(wave);
             const int b = lane / 16, jj = lane % 16;
             float xv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float acc = (r == jj) ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= As[(16 * b + r) * AS + 16 * b + i] * xv[i];
+                for (int i = 0; i < r; ++i) acc -= Ah[(16 * b + r) * AS + 16 * b + i] * xv[i];
                 xv[r] = acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Ts[(16 * b + r) * AS + 16 * b + jj] = xv[r];
-        } else {
-            for (int e = tid - 64; e < kC * kC; e += 192) {
-                const int r = e / kC, c = e % kC;
-                if ((r / 16) != (c / 16)) Ts[r * AS + c] = 0.f;
+            for (int r = 0; r < 16; ++r) Th[(16 * b + r) * AS + 16 * b + jj] = xv[r];
+        } else if (wave >= 2) {
+            for (int e = tid - 128; e < nh * 2 * 256; e += 128) {
+                const int hh = e / 512, t = (e / 256) % 2, r = (e / 16) % 16, c = e % 16;
+                TS_OF(hh)[(32 * t + r) * AS + 32 * t + 16 + c] = 0.f;
             }
         }
-        __syncthreads();
-        // Phase 2: row blocks b = 1..3; wave j < b makes tile (b, j):
-        //   rhs = -A[b, j..b-1] Tinv[j..b-1, j];  Tinv[b, j] = Tinv[b, b] rhs   (fp32 MFMA)
-        for (int b = 1; b < 4; ++b) {
-            if (wave < b) {
-                const int j = wave;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int k0 = 16 * j; k0 < 16 * b; k0 += 4) {
-                    const float a = As[(16 * b + lane % 16) * AS + k0 + lane / 16];
-                    const float t = Ts[(k0 + lane / 16) * AS + 16 * j + lane % 16];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, t, acc, 0, 0, 0);
+        __syncthreads();  // diagonal blocks complete
+
+        // Tinv[b1][b0] = -Tinv[b1][b1] (A[b1][b0] Tinv[b0][b0]) for (b1, b0) = (1, 0), (3, 2):
+        // wave = 2 hh + p takes p = 0, 1 of head slot hh.
+        const int hw = wave / 2, pw = wave % 2;
+        if (hw < nh) {
+            const float *Ah = AS_OF(hw);
+            float *Th = TS_OF(hw);
+            const int b0 = 2 * pw, b1 = b0 + 1;
+            f32x4 rhs = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const float av = Ah[(16 * b1 + cc) * AS + 16 * b0 + 4 * s4 + g4];
+                const float bv = Th[(16 * b0 + 4 * s4 + g4) * AS + 16 * b0 + cc];
+                rhs = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, rhs, 0, 0, 0);
+            }
+            // rhs as the B operand: step s supplies k = 4 g + s, i.e. this lane's entry s
+            f32x4 out = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const float av = Th[(16 * b1 + cc) * AS + 16 * b1 + 4 * g4 + s4];
+                out = __builtin_amdgcn_mfma_f32_16x16x4f32(av, rhs[s4], out, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Th[(16 * b1 + 4 * g4 + i) * AS + 16 * b0 + cc] = -out[i];
+        }
+        __syncthreads();  // blocks (1,0) and (3,2) complete
+
+        // Lower-left 32 x 32 block: W_i = sum_{l = jc..1} A[i][l] Tinv[l][jc] (i = 2, 3), then
+        // Tinv[2][jc] = -Tinv[2][2] W_2, Tinv[3][jc] = -(Tinv[3][2] W_2 + Tinv[3][3] W_3).
+        // wave = 2 hh + jc.
+        if (hw < nh) {
+            const float *Ah = AS_OF(hw);
+            float *Th = TS_OF(hw);
+            const int jc = pw;
+            f32x4 W2 = {0.f, 0.f, 0.f, 0.f}, W3 = {0.f, 0.f, 0.f, 0.f};
+            for (int l = jc; l < 2; ++l) {
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const float tv = Th[(16 * l + 4 * s4 + g4) * AS + 16 * jc + cc];
+                    const float a2 = Ah[(32 + cc) * AS + 16 * l + 4 * s4 + g4];
+                    const float a3 = Ah[(48 + cc) * AS + 16 * l + 4 * s4 + g4];
+                    W2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, tv, W2, 0, 0, 0);
+                    W3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, tv, W3, 0, 0, 0);
                 }
-                float *R = Rs[wave];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) R[(4 * (lane / 16) + i) * RS + lane % 16] = -acc[i];
-                f32x4 out = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4) {
-                    const float a = Ts[(16 * b + lane % 16) * AS + 16 * b + k0 + lane / 16];
-                    const float r = R[(k0 + lane / 16) * RS + lane % 16];
-                    out = __builtin_amdgcn_mfma_f32_16x16x4f32(a, r, out, 0, 0, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    Ts[(16 * b + 4 * (lane / 16) + i) * AS + 16 * j + lane % 16] = out[i];
             }
-            __syncthreads();
-        }
-        // M into LDS over A (no longer needed), then Tinv and M to the workspace as fragments
+            f32x4 T2 = {0.f, 0.f, 0.f, 0.f}, T3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const int kc = 4 * g4 + s4;
+                T2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[(32 + cc) * AS + 32 + kc], W2[s4], T2, 0, 0, 0);
+                T3 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[(48 + cc) * AS + 32 + kc], W2[s4], T3, 0, 0, 0);
+                T3 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[(48 + cc) * AS + 48 + kc], W3[s4], T3, 0, 0, 0);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                As[(16 * wave + 4 * (lane / 16) + i) * AS + 16 * j + lane % 16] = mreg[j][i];
-        __syncthreads();
-        {
-            _Float16 *Tg = ws.Tm + ((int64_t)sub * Hv + h) * kPackedTri;
-            _Float16 *Mg = ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
-            for (int c = tid; c < 2 * kTriFrags * 64; c += 256) {
-                const int which = c / (kTriFrags * 64), cf = c % (kTriFrags * 64);
-                const int f = cf / 64, l = cf % 64;
-                const int w = f < 2 ? f : 2 + (f - 2) / 2, kb = f < 2 ? 0 : (f - 2) % 2;
-                const float *src = (which ? As : Ts) + (16 * w + l % 16) * AS + 32 * kb + 8 * (l / 16);
-                half8 hv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) hv[e] = (_Float16)src[e];
-                *(half8 *)((which ? Mg : Tg) + cf * 8) = hv;
+            for (int i = 0; i < 4; ++i) {
+                Th[(32 + 4 * g4 + i) * AS + 16 * jc + cc] = -T2[i];
+                Th[(48 + 4 * g4 + i) * AS + 16 * jc + cc] = -T3[i];
             }
         }
-        __syncthreads();
+        __syncthreads();  // Tinv complete
+
+        // Tinv to the workspace as fragments, with the column order of the M fragments
+        for (int c = tid; c < nh * kTriFrags * 64; c += 256) {
+            const int hh = c / (kTriFrags * 64), f = (c / 64) % kTriFrags, l = c % 64;
+            const int w = f < 2 ? f : 2 + (f - 2) / 2, kb = f < 2 ? 0 : (f - 2) % 2;
+            const float *src = TS_OF(hh) + (16 * w + l % 16) * AS + 32 * kb + 4 * (l / 16);
+            const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 16);
+            half8 hv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hv[e] = (_Float16)lo[e];
+                hv[4 + e] = (_Float16)hi[e];
+            }
+            const int h = kh * group + hp + hh;
+            *(half8 *)(ws.Tm + ((int64_t)sub * Hv + h) * kPackedTri + (f * 64 + l) * 8) = hv;
+        }
+        if (hp + 2 < group) __syncthreads();  // A, Tinv and the gates are reused by the next pair
     }
+#undef AS_OF
+#undef TS_OF
 }
 
 // Per-lane register set of one sub-chunk's chain inputs.  Compute wave w handles rows
@@ -518,6 +574,10 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
     StepRegs<D, Act> &C = R[K];
     const int wave = a.wave, col = a.col, kg = a.kg, lane = a.kg * 16 + a.col;
     const int r0 = 16 * wave + 4 * kg;
+    // Tinv and M fragments order their 32-wide K steps as (4 rows of tile 2kb, 4 rows of tile
+    // 2kb+1) per lane group; rt and dt hold the rows of R and D in that order, so that their
+    // B fragments stay 16 contiguous bytes: row 16w + 4kg + i sits at position pr0 + i.
+    const int pr0 = 32 * (wave / 2) + 8 * kg + 4 * (wave % 2);
     const float *F = L.fac[cl & 1];
     step_issue<D, Act>(R[(K + 2) % 3], a, min(cl + 2, nsub - 1), ws);
 
@@ -546,7 +606,7 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
             rv[i] = (_Float16)(fb[i] * v - fbg[i] * X[i]);
             Ob[i] = fg[i] * P[i];
         }
-        *(half4 *)(L.rt + col * TS + r0) = rv;
+        *(half4 *)(L.rt + col * TS + pr0) = rv;
     }
     __syncthreads();  // #1: rt complete; xvr, K and the other factor buffer are free
 
@@ -569,7 +629,7 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
             dv[i] = (_Float16)Dl[i];
             ddv[i] = (_Float16)(fd[i] * Dl[i]);
         }
-        *(half4 *)(L.dt + col * TS + r0) = dv;
+        *(half4 *)(L.dt + col * TS + pr0) = dv;
         *(half4 *)(L.ddt + col * TS + r0) = ddv;
     }
     __syncthreads();  // #2: dt, ddt and K complete
