@@ -570,7 +570,6 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
     using SR = StepRegs<D, Act>;
     constexpr int HS = CL::HS, TS = CL::TS, ST = CL::ST;
     constexpr int TPW = D / 64;  // d_k tiles per wave
-    if (cl >= nsub) return;
     StepRegs<D, Act> &C = R[K];
     const int wave = a.wave, col = a.col, kg = a.kg, lane = a.kg * 16 + a.col;
     const int r0 = 16 * wave + 4 * kg;
@@ -751,11 +750,16 @@ __global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__res
         L.xvr[a.tid] = L.xvr[a.tid] | *(const u32x4 *)(win + (int64_t)vr * a.C + a.vch + cc);
     }
     __syncthreads();
-    for (int cl = 0; cl < nsub; cl += 3) {
+    // Whole triples of steps first, with no exits inside: every load issued in the loop is
+    // then consumed on every path, and the compiler's waits stay two steps behind the loads.
+    int cl = 0;
+    for (; cl + 3 <= nsub; cl += 3) {
         chain_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, S, w0, w1, w2, w3, scale, ws);
         chain_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, S, w0, w1, w2, w3, scale, ws);
         chain_step<2, D, Act, Out, SILU>(L, R, a, cl + 2, nsub, S, w0, w1, w2, w3, scale, ws);
     }
+    if (cl < nsub) chain_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, S, w0, w1, w2, w3, scale, ws);
+    if (cl + 1 < nsub) chain_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, S, w0, w1, w2, w3, scale, ws);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int kt = wave * TPW + t;
