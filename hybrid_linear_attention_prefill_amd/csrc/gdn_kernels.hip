@@ -137,6 +137,22 @@ __device__ __forceinline__ void load8(const u32x4 *row, int cl, float (&v)[8])
     }
 }
 
+// Sum over aligned groups of N lanes (N = 8 or 16), the result in every lane of the group:
+// a butterfly of DPP moves (quad permutations, then the half-row and row mirrors).
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N == 8 || N == 16, "group of 8 or 16 lanes");
+#define GDN_DPP_ADD(ctrl) \
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xf, 0xf, false))
+    GDN_DPP_ADD(0xb1);   // quad_perm [1, 0, 3, 2]
+    GDN_DPP_ADD(0x4e);   // quad_perm [2, 3, 0, 1]
+    GDN_DPP_ADD(0x141);  // row_half_mirror
+    if constexpr (N == 16) GDN_DPP_ADD(0x140);  // row_mirror
+#undef GDN_DPP_ADD
+    return v;
+}
+
 // ------------------------------------------------------------------------------------------
 // prep_kernel: state-independent factors of one (sub-chunk, key head).
 // ------------------------------------------------------------------------------------------
@@ -229,19 +245,29 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
                 for (int j = 0; j < 4; ++j) w[e][j] = to_f32(wv[e * 4 + j]);
         }
         _Float16 *dstl = part ? k16 : q16;
+        // rows rp*RPT .. +RPT-1; the conv reads raw rows r .. r+3, kept as a rolling window
+        float xw[4][8];
+        if (conv_on) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) load8<Act>(xs + (rp * RPT + j) * XSC, cl, xw[j + 1]);
+        }
 #pragma unroll
         for (int ri = 0; ri < RPT; ++ri) {
             const int r = rp * RPT + ri;
             float y[8];
             if (conv_on) {
-                float xv[4][8];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) load8<Act>(xs + (r + j) * XSC, cl, xv[j]);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float a = w[e][0] * xv[0][e] + w[e][1] * xv[1][e] + w[e][2] * xv[2][e] +
-                              w[e][3] * xv[3][e];
-                    if constexpr (SILU) a = a / (1.f + expf(-a));
+                    xw[0][e] = xw[1][e];
+                    xw[1][e] = xw[2][e];
+                    xw[2][e] = xw[3][e];
+                }
+                load8<Act>(xs + (r + 3) * XSC, cl, xw[3]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float a = w[e][0] * xw[0][e] + w[e][1] * xw[1][e] + w[e][2] * xw[2][e] +
+                              w[e][3] * xw[3][e];
+                    if constexpr (SILU) a = a / (1.f + __expf(-a));
                     y[e] = a;
                 }
             } else {
@@ -250,9 +276,8 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
-#pragma unroll
-            for (int off = 1; off < G8 / 2; off <<= 1) ss += __shfl_xor(ss, off);
-            const float inv = (r < nv) ? 1.0f / sqrtf(ss + eps) : 0.f;
+            ss = group_sum<G8 / 2>(ss);
+            const float inv = (r < nv) ? __builtin_amdgcn_rsqf(ss + eps) : 0.f;
             half8 hv;
 #pragma unroll
             for (int e = 0; e < 8; ++e) hv[e] = (_Float16)(y[e] * inv);
@@ -312,12 +337,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             Gs[wave][r] = gv;
             bs[wave][r] = bv;
             const float Gn = __shfl(gv, 63);
-            const float gam = expf(gv);
+            const float gam = __expf(gv);
             float *F = ws.Fac + ((int64_t)sub * Hv + h) * 4 * kC;
             F[r] = bv;
             F[kC + r] = bv * gam;
             F[2 * kC + r] = gam;
-            F[3 * kC + r] = expf(Gn - gv);
+            F[3 * kC + r] = __expf(Gn - gv);
         }
         __syncthreads();  // gates ready; raw rows, q16 and k16 are no longer read
 
@@ -338,7 +363,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int c = 16 * j + 4 * g4 + i;
-                        const float dec = (c <= row) ? expf(Gr - Gc[i]) : 0.f;
+                        const float dec = (c <= row) ? __expf(Gr - Gc[i]) : 0.f;
                         mt[j][i] = qk[j][i] * dec;
                         at[i] = (c < row) ? br * kk[j][i] * dec : 0.f;
                     }
