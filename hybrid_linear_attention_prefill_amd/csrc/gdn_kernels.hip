@@ -117,6 +117,8 @@ __device__ __forceinline__ int find_seg(const SegArgs &sa, int sub)
 // every column of the K step lies above the diagonal of row tile w (the fragment is zero).
 __device__ __forceinline__ int tri_frag(int w, int kb) { return kb == 0 ? (w < 2 ? w : 2 * w - 2) : (w < 2 ? -1 : 2 * w - 1); }
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <typename Act>
 __device__ __forceinline__ void load8(const u32x4 *row, int cl, float (&v)[8])
 {
@@ -157,7 +159,7 @@ __device__ __forceinline__ float group_sum(float v)
 // prep_kernel: state-independent factors of one (sub-chunk, key head).
 // ------------------------------------------------------------------------------------------
 template <int D, typename Act, bool SILU>
-__global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__restrict__ x,
+__global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__restrict__ x,
                                                       const Act *__restrict__ conv_w, int conv_on,
                                                       const float *__restrict__ g,
                                                       const float *__restrict__ beta, int Hk,
@@ -172,21 +174,24 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
     constexpr int LPT = (NCHUNK + 255) / 256;
     constexpr int XSC = CPR + 1;                // LDS row stride of raw x, in chunks
     constexpr int HS = D + 8;                   // fp16 row stride of q, k
-    constexpr int AS = kC + 4;                  // fp32 row stride of A, Tinv
     constexpr int XBYTES = XR * XSC * 16;
     constexpr int QBYTES = kC * HS * 2;
-    constexpr int TBYTES = kC * AS * 4;         // one 64 x 64 fp32 factor
-    constexpr int P13 = XBYTES + 2 * QBYTES;
-    constexpr int UBYTES = P13 > 4 * TBYTES ? P13 : 4 * TBYTES;
-    // Phases 1-3 use raw x rows, q16 and k16; phase 4 reuses the same bytes for A and Tinv of
-    // two value heads.
+    // A and Tinv of a value head are kept as their ten lower 16x16 blocks (b, j), j <= b,
+    // block index b (b + 1) / 2 + j, rows of 20 floats, blocks 324 floats apart (the four
+    // diagonal blocks then start in different LDS banks).
+    constexpr int BROW = 20, BSTR = 16 * BROW + 4;
+    constexpr int MBYTES = 10 * BSTR * 4;
+    constexpr int UBYTES = cmax(cmax(XBYTES, 2 * QBYTES), 4 * MBYTES);
+    // Phase 1 keeps the raw x rows, phases 2-3 q16 and k16 over the same bytes, phase 4 A and
+    // Tinv of two value heads over them again.
     __shared__ __attribute__((aligned(16))) unsigned char ubuf[UBYTES];
     __shared__ __attribute__((aligned(16))) float Gs[2][kC], bs[2][kC];
     u32x4 *const xs = (u32x4 *)ubuf;
-    _Float16 *const q16 = (_Float16 *)(ubuf + XBYTES);
+    _Float16 *const q16 = (_Float16 *)ubuf;
     _Float16 *const k16 = q16 + kC * HS;
-#define AS_OF(hh) ((float *)(ubuf + (hh) * TBYTES))
-#define TS_OF(hh) ((float *)(ubuf + (2 + (hh)) * TBYTES))
+#define AS_OF(hh) ((float *)(ubuf + (hh) * MBYTES))
+#define TS_OF(hh) ((float *)(ubuf + (2 + (hh)) * MBYTES))
+#define BLK(b, j) (((b) * ((b) + 1) / 2 + (j)) * BSTR)
 
     const int sub = blockIdx.x, kh = blockIdx.y;
     const int s = find_seg(sa, sub);
@@ -247,6 +252,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
         _Float16 *dstl = part ? k16 : q16;
         // rows rp*RPT .. +RPT-1; the conv reads raw rows r .. r+3, kept as a rolling window
         float xw[4][8];
+        half8 outv[RPT];
         if (conv_on) {
 #pragma unroll
             for (int j = 0; j < 3; ++j) load8<Act>(xs + (rp * RPT + j) * XSC, cl, xw[j + 1]);
@@ -278,11 +284,12 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             for (int e = 0; e < 8; ++e) ss += y[e] * y[e];
             ss = group_sum<G8 / 2>(ss);
             const float inv = (r < nv) ? __builtin_amdgcn_rsqf(ss + eps) : 0.f;
-            half8 hv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) hv[e] = (_Float16)(y[e] * inv);
-            *(half8 *)(dstl + r * HS + cd) = hv;
+            for (int e = 0; e < 8; ++e) outv[ri][e] = (_Float16)(y[e] * inv);
         }
+        __syncthreads();  // raw rows no longer read; q16 and k16 take their bytes
+#pragma unroll
+        for (int ri = 0; ri < RPT; ++ri) *(half8 *)(dstl + (rp * RPT + ri) * HS + cd) = outv[ri];
     }
     __syncthreads();
 
@@ -367,7 +374,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
                         mt[j][i] = qk[j][i] * dec;
                         at[i] = (c < row) ? br * kk[j][i] * dec : 0.f;
                     }
-                    *(f32x4 *)(AS_OF(hh) + row * AS + 16 * j + 4 * g4) = at;
+                    *(f32x4 *)(AS_OF(hh) + BLK(wave, j) + cc * BROW + 4 * g4) = at;
                 }
             }
             _Float16 *Mg = ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
@@ -384,8 +391,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
         __syncthreads();  // A complete
 
         // Tinv = (I + A)^-1 by 16 x 16 blocks.  Diagonal blocks by forward substitution
-        // (wave hh, lane = 16 b + column); the upper blocks that the fragments cover,
-        // (0,1) and (2,3), are cleared by waves 2 and 3.
+        // (wave hh, lane = 16 b + column).
         if (wave < nh) {
             const float *Ah = AS_OF(wave);
             float *Th = TS_OF(wave);
@@ -395,16 +401,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             for (int r = 0; r < 16; ++r) {
                 float acc = (r == jj) ? 1.f : 0.f;
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= Ah[(16 * b + r) * AS + 16 * b + i] * xv[i];
+                for (int i = 0; i < r; ++i) acc -= Ah[BLK(b, b) + r * BROW + i] * xv[i];
                 xv[r] = acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) Th[(16 * b + r) * AS + 16 * b + jj] = xv[r];
-        } else if (wave >= 2) {
-            for (int e = tid - 128; e < nh * 2 * 256; e += 128) {
-                const int hh = e / 512, t = (e / 256) % 2, r = (e / 16) % 16, c = e % 16;
-                TS_OF(hh)[(32 * t + r) * AS + 32 * t + 16 + c] = 0.f;
-            }
+            for (int r = 0; r < 16; ++r) Th[BLK(b, b) + r * BROW + jj] = xv[r];
         }
         __syncthreads();  // diagonal blocks complete
 
@@ -418,19 +419,19 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             f32x4 rhs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const float av = Ah[(16 * b1 + cc) * AS + 16 * b0 + 4 * s4 + g4];
-                const float bv = Th[(16 * b0 + 4 * s4 + g4) * AS + 16 * b0 + cc];
+                const float av = Ah[BLK(b1, b0) + cc * BROW + 4 * s4 + g4];
+                const float bv = Th[BLK(b0, b0) + (4 * s4 + g4) * BROW + cc];
                 rhs = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, rhs, 0, 0, 0);
             }
             // rhs as the B operand: step s supplies k = 4 g + s, i.e. this lane's entry s
             f32x4 out = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                const float av = Th[(16 * b1 + cc) * AS + 16 * b1 + 4 * g4 + s4];
+                const float av = Th[BLK(b1, b1) + cc * BROW + 4 * g4 + s4];
                 out = __builtin_amdgcn_mfma_f32_16x16x4f32(av, rhs[s4], out, 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Th[(16 * b1 + 4 * g4 + i) * AS + 16 * b0 + cc] = -out[i];
+            for (int i = 0; i < 4; ++i) Th[BLK(b1, b0) + (4 * g4 + i) * BROW + cc] = -out[i];
         }
         __syncthreads();  // blocks (1,0) and (3,2) complete
 
@@ -445,9 +446,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
             for (int l = jc; l < 2; ++l) {
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
-                    const float tv = Th[(16 * l + 4 * s4 + g4) * AS + 16 * jc + cc];
-                    const float a2 = Ah[(32 + cc) * AS + 16 * l + 4 * s4 + g4];
-                    const float a3 = Ah[(48 + cc) * AS + 16 * l + 4 * s4 + g4];
+                    const float tv = Th[BLK(l, jc) + (4 * s4 + g4) * BROW + cc];
+                    const float a2 = Ah[BLK(2, l) + cc * BROW + 4 * s4 + g4];
+                    const float a3 = Ah[BLK(3, l) + cc * BROW + 4 * s4 + g4];
                     W2 = __builtin_amdgcn_mfma_f32_16x16x4f32(a2, tv, W2, 0, 0, 0);
                     W3 = __builtin_amdgcn_mfma_f32_16x16x4f32(a3, tv, W3, 0, 0, 0);
                 }
@@ -456,14 +457,14 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
                 const int kc = 4 * g4 + s4;
-                T2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[(32 + cc) * AS + 32 + kc], W2[s4], T2, 0, 0, 0);
-                T3 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[(48 + cc) * AS + 32 + kc], W2[s4], T3, 0, 0, 0);
-                T3 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[(48 + cc) * AS + 48 + kc], W3[s4], T3, 0, 0, 0);
+                T2 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[BLK(2, 2) + cc * BROW + kc], W2[s4], T2, 0, 0, 0);
+                T3 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[BLK(3, 2) + cc * BROW + kc], W2[s4], T3, 0, 0, 0);
+                T3 = __builtin_amdgcn_mfma_f32_16x16x4f32(Th[BLK(3, 3) + cc * BROW + kc], W3[s4], T3, 0, 0, 0);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                Th[(32 + 4 * g4 + i) * AS + 16 * jc + cc] = -T2[i];
-                Th[(48 + 4 * g4 + i) * AS + 16 * jc + cc] = -T3[i];
+                Th[BLK(2, jc) + (4 * g4 + i) * BROW + cc] = -T2[i];
+                Th[BLK(3, jc) + (4 * g4 + i) * BROW + cc] = -T3[i];
             }
         }
         __syncthreads();  // Tinv complete
@@ -472,8 +473,11 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
         for (int c = tid; c < nh * kTriFrags * 64; c += 256) {
             const int hh = c / (kTriFrags * 64), f = (c / 64) % kTriFrags, l = c % 64;
             const int w = f < 2 ? f : 2 + (f - 2) / 2, kb = f < 2 ? 0 : (f - 2) % 2;
-            const float *src = TS_OF(hh) + (16 * w + l % 16) * AS + 32 * kb + 4 * (l / 16);
-            const f32x4 lo = *(const f32x4 *)src, hi = *(const f32x4 *)(src + 16);
+            const float *Th = TS_OF(hh);
+            const int off = (l % 16) * BROW + 4 * (l / 16);
+            const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};  // blocks above the diagonal
+            const f32x4 lo = (2 * kb <= w) ? *(const f32x4 *)(Th + BLK(w, 2 * kb) + off) : z4;
+            const f32x4 hi = (2 * kb + 1 <= w) ? *(const f32x4 *)(Th + BLK(w, 2 * kb + 1) + off) : z4;
             half8 hv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -487,6 +491,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(SegArgs sa, const Act *__r
     }
 #undef AS_OF
 #undef TS_OF
+#undef BLK
 }
 
 // Per-lane register set of one sub-chunk's chain inputs.  Compute wave w handles rows
