@@ -799,6 +799,28 @@ __global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__res
             S_out[((int64_t)h * D + k) * D + a.c0 + col] = S[t][i];
         }
     }
+    // The new conv window: rows n .. n+2 of (window ++ x), per channel.  This workgroup
+    // rewrites the 16 v channels whose old window it read above, and one slice of the q | k
+    // channels (whose old window only the prep kernel read, before this kernel started).  Each
+    // thread takes one channel and reads its three values before writing them back.
+    Act *win_out = (Act *)sa.seg[s].win_out;
+    if (conv_on && win_out != nullptr) {
+        const int nqk = 2 * Hk * D, per = (nqk + n_units - 1) / n_units;
+        const int t = threadIdx.x;
+        int ch = -1;
+        if (t < 16) ch = a.vch + t;
+        else if (t < 16 + per && unit * per + (t - 16) < nqk) ch = unit * per + (t - 16);
+        if (ch >= 0) {
+            Act v[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const int64_t r = (int64_t)a.seg_n + i;
+                v[i] = (r < 3) ? win[r * a.C + ch] : x[(a.seg_row0 + r - 3) * a.C + ch];
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) win_out[(int64_t)i * a.C + ch] = v[i];
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -887,7 +909,6 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
                      hipStream_t st, const EventMarks &em)
 {
     const int conv_on = d.conv_width > 0 ? 1 : 0;
-    const int C = 2 * d.n_k_heads * D + d.n_v_heads * D;
     em.mark(0);
     if (d.conv_silu && conv_on)
         hipLaunchKernelGGL((prep_kernel<D, Act, true>), dim3(sa.n_sub, d.n_k_heads), dim3(256), 0, st,
@@ -908,10 +929,7 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
                            dim3(256), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
                            d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
     em.mark(3);
-    em.mark(4);
-    if (conv_on)
-        hipLaunchKernelGGL((window_kernel<Act>), dim3((C + 255) / 256, sa.n_seg), dim3(256), 0, st,
-                           sa, (const Act *)x, C);
+    em.mark(4);  // the conv window is written by the chain kernel
     em.mark(5);
     return (int)hipGetLastError();
 }
