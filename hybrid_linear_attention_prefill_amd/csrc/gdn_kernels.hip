@@ -67,18 +67,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
 __device__ __forceinline__ void store_out(float *p, float v) { *p = v; }
 __device__ __forceinline__ void store_out(bf16_t *p, float v) { p->bits = f32_to_bf16_bits(v); }
 
-// Store one output element at element offset `off` of a raw buffer (dropped out of range).
+// Store four adjacent output elements starting at element offset `off` (a multiple of 4) of a
+// raw buffer; dropped when out of range.
 template <typename Out>
-__device__ __forceinline__ void store_out_buf(__amdgpu_buffer_rsrc_t r, int off, float v);
+__device__ __forceinline__ void store_out4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v);
 template <>
-__device__ __forceinline__ void store_out_buf<float>(__amdgpu_buffer_rsrc_t r, int off, float v)
+__device__ __forceinline__ void store_out4<float>(__amdgpu_buffer_rsrc_t r, int off, f32x4 v)
 {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off * 4, 0, 0);
 }
 template <>
-__device__ __forceinline__ void store_out_buf<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, float v)
+__device__ __forceinline__ void store_out4<bf16_t>(__amdgpu_buffer_rsrc_t r, int off, f32x4 v)
 {
-    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(v), r, off * 2, 0, 0);
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 w = {(uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                     (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off * 2, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
@@ -522,42 +526,53 @@ struct ChainArgs {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-template <int D, typename Act>
+// Prefetch of one sub-chunk's chain inputs into register set R, in parts so that a step
+// spreads its loads over its length (one batch of fourteen 1 KB loads from every wave at once
+// stalls the waves at issue): PART 0 the raw v rows and factors (consumed one step later), 1
+// the K fragments, 2 the Q fragments, 3 the Tinv and M fragments; -1 all of them.
+template <int D, typename Act, int PART>
 __device__ __forceinline__ void step_issue(StepRegs<D, Act> &R, const ChainArgs &a, int cl,
                                            const Workspace &ws)
 {
     using SR = StepRegs<D, Act>;
     const int sub = a.sub0 + cl, rb = cl * kC;
     const int lane = 16 * a.kg + a.col;
-    const half8 *Kg = (const half8 *)(ws.Kh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
-    const half8 *Qg = (const half8 *)(ws.Qh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
+    if constexpr (PART == 0 || PART == -1) {
+        const u32x4 *Fg = (const u32x4 *)(ws.Fac + ((int64_t)sub * a.Hv + a.h) * 4 * kC);
 #pragma unroll
-    for (int kb = 0; kb < SR::KB; ++kb) {
-        R.kf[kb] = Kg[kb * 64];
-        R.qf[kb] = Qg[kb * 64];
+        for (int i = 0; i < SR::LP; ++i) {
+            const int idx = a.tid + 256 * i;
+            if (idx < SR::VC) {
+                const int vr = idx / SR::VCR, cc = (idx % SR::VCR) * SR::EPC;
+                const int sr = rb + vr - 3;  // sequence-local row (rows before 0: the window, added apart)
+                R.ld[i] = __builtin_amdgcn_raw_buffer_load_b128(a.rx, (sr * a.C + a.vch + cc) * (int)sizeof(Act), 0, 0);
+            } else {
+                R.ld[i] = Fg[min(idx - SR::VC, 63)];
+            }
+        }
     }
-    const half8 *Tg = (const half8 *)(ws.Tm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
-    const half8 *Mg = (const half8 *)(ws.Mm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
-    const half8 z = {};
-    R.tf[0] = Tg[64 * tri_frag(a.wave, 0)];
-    R.mf[0] = Mg[64 * tri_frag(a.wave, 0)];
-    if (a.wave >= 2) {  // wave-uniform
-        R.tf[1] = Tg[64 * tri_frag(a.wave, 1)];
-        R.mf[1] = Mg[64 * tri_frag(a.wave, 1)];
-    } else {
-        R.tf[1] = z;
-        R.mf[1] = z;
-    }
-    const u32x4 *Fg = (const u32x4 *)(ws.Fac + ((int64_t)sub * a.Hv + a.h) * 4 * kC);
+    if constexpr (PART == 1 || PART == -1) {
+        const half8 *Kg = (const half8 *)(ws.Kh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
 #pragma unroll
-    for (int i = 0; i < SR::LP; ++i) {
-        const int idx = a.tid + 256 * i;
-        if (idx < SR::VC) {
-            const int vr = idx / SR::VCR, cc = (idx % SR::VCR) * SR::EPC;
-            const int sr = rb + vr - 3;  // sequence-local row (rows before 0: the window, added apart)
-            R.ld[i] = __builtin_amdgcn_raw_buffer_load_b128(a.rx, (sr * a.C + a.vch + cc) * (int)sizeof(Act), 0, 0);
+        for (int kb = 0; kb < SR::KB; ++kb) R.kf[kb] = Kg[kb * 64];
+    }
+    if constexpr (PART == 2 || PART == -1) {
+        const half8 *Qg = (const half8 *)(ws.Qh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
+#pragma unroll
+        for (int kb = 0; kb < SR::KB; ++kb) R.qf[kb] = Qg[kb * 64];
+    }
+    if constexpr (PART == 3 || PART == -1) {
+        const half8 *Tg = (const half8 *)(ws.Tm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
+        const half8 *Mg = (const half8 *)(ws.Mm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
+        const half8 z = {};
+        R.tf[0] = Tg[64 * tri_frag(a.wave, 0)];
+        R.mf[0] = Mg[64 * tri_frag(a.wave, 0)];
+        if (a.wave >= 2) {  // wave-uniform
+            R.tf[1] = Tg[64 * tri_frag(a.wave, 1)];
+            R.mf[1] = Mg[64 * tri_frag(a.wave, 1)];
         } else {
-            R.ld[i] = Fg[min(idx - SR::VC, 63)];
+            R.tf[1] = z;
+            R.mf[1] = z;
         }
     }
 }
@@ -608,7 +623,8 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
     // B fragments stay 16 contiguous bytes: row 16w + 4kg + i sits at position pr0 + i.
     const int pr0 = 32 * (wave / 2) + 8 * kg + 4 * (wave % 2);
     const float *F = L.fac[cl & 1];
-    step_issue<D, Act>(R[(K + 2) % 3], a, min(cl + 2, nsub - 1), ws);
+    const int cn = min(cl + 2, nsub - 1);  // the sub-chunk whose inputs this step prefetches
+    step_issue<D, Act, 1>(R[(K + 2) % 3], a, cn, ws);
 
     // X = K S and P = Q S for row tile `wave`
     f32x4 X = {0.f, 0.f, 0.f, 0.f}, P = {0.f, 0.f, 0.f, 0.f};
@@ -616,14 +632,14 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
     for (int kb = 0; kb < SR::KB; ++kb) {
         const half8 bS = *(const half8 *)(L.s16t + col * ST + 32 * kb + 8 * kg);
         X = mfma16(C.kf[kb], bS, X);
-        P = mfma16(C.qf[kb], bS, P);
+        P = mfma16(bS, C.qf[kb], P);  // P transposed: this lane's row, four adjacent columns
     }
     // R = beta V - beta gamma X; the state part of O is gamma P
     f32x4 Ob;
     {
         const Act *vrows = (const Act *)L.xvr;
         const f32x4 fb = *(const f32x4 *)(F + r0), fbg = *(const f32x4 *)(F + kC + r0);
-        const f32x4 fg = *(const f32x4 *)(F + 2 * kC + r0);
+        const float fg = F[2 * kC + 16 * wave + col];  // gamma of row 16 wave + col
         float vr[7];
 #pragma unroll
         for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * 16 + col]);
@@ -633,10 +649,11 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
             float v = w0 * vr[i] + w1 * vr[i + 1] + w2 * vr[i + 2] + w3 * vr[i + 3];
             if constexpr (SILU) v = v / (1.f + expf(-v));
             rv[i] = (_Float16)(fb[i] * v - fbg[i] * X[i]);
-            Ob[i] = fg[i] * P[i];
+            Ob[i] = fg * P[i];
         }
         *(half4 *)(L.rt + col * TS + pr0) = rv;
     }
+    step_issue<D, Act, 0>(R[(K + 2) % 3], a, cn, ws);
     __syncthreads();  // #1: rt complete; xvr, K and the other factor buffer are free
 
     // this step's K rows into LDS for the state update; next step's v rows and factors
@@ -661,6 +678,7 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
         *(half4 *)(L.dt + col * TS + pr0) = dv;
         *(half4 *)(L.ddt + col * TS + r0) = ddv;
     }
+    step_issue<D, Act, 2>(R[(K + 2) % 3], a, cn, ws);
     __syncthreads();  // #2: dt, ddt and K complete
 
     // S' = gamma_n S + K^T (exp(G_n - G) D)
@@ -685,14 +703,15 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
     }
     // O = scale (gamma Q S + M D)
     {
+        // transposed product (D^T M^T): this lane gets row 16 wave + col, columns 4 kg .. +3
         f32x4 Oa = Ob;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-            Oa = mfma16(C.mf[kb], *(const half8 *)(L.dt + col * TS + 32 * kb + 8 * kg), Oa);
-        const int obase = ((cl * kC + r0) * a.Hv + a.h) * D + a.c0 + col;  // element offset
-#pragma unroll
-        for (int i = 0; i < 4; ++i) store_out_buf<Out>(a.ro, obase + i * a.Hv * D, scale * Oa[i]);
+            Oa = mfma16(*(const half8 *)(L.dt + col * TS + 32 * kb + 8 * kg), C.mf[kb], Oa);
+        const int obase = ((cl * kC + 16 * wave + col) * a.Hv + a.h) * D + a.c0 + 4 * kg;
+        store_out4<Out>(a.ro, obase, Oa * scale);
     }
+    step_issue<D, Act, 3>(R[(K + 2) % 3], a, cn, ws);
     __syncthreads();  // #3: s16t complete for the next step
 }
 
@@ -756,8 +775,8 @@ __global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__res
     }
     StepRegs<D, Act> R[3];
     if (nsub > 0) {
-        step_issue<D, Act>(R[0], a, 0, ws);
-        step_issue<D, Act>(R[1], a, min(1, nsub - 1), ws);
+        step_issue<D, Act, -1>(R[0], a, 0, ws);
+        step_issue<D, Act, -1>(R[1], a, min(1, nsub - 1), ws);
     }
     f32x4 S[TPW];
 #pragma unroll
