@@ -164,8 +164,9 @@ gdn_status gdn_prefill_chunked(const gdn_desc *desc, const void *x, const void *
 /* gdn_prefill_chunked plus per-kernel timing, for benchmarks.  events[0 .. n_events) are
  * hipEvent_t handles the caller created with timing enabled; the library records
  * events[2k] before and events[2k+1] after the k-th kernel it enqueues on `stream`
- * (k = 0 prep, 1 chain, 2 window; pairs past n_events / 2 are not recorded).  Results and
- * errors are those of gdn_prefill_chunked. */
+ * (k = 0 the prep kernel, 1 the chain kernel, which also writes the new conv window; pair 2
+ * is recorded back to back and brackets no kernel; pairs past n_events / 2 are not
+ * recorded).  Results and errors are those of gdn_prefill_chunked. */
 gdn_status gdn_prefill_chunked_events(const gdn_desc *desc, const void *x, const void *conv_w,
                                       const float *g, const float *beta, const gdn_state *in,
                                       gdn_state *out, void *o, int64_t T, int32_t mode,
