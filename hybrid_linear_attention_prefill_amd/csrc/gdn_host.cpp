@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdint>
 #include <cstring>
 #include <vector>
 
@@ -44,6 +45,10 @@ Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base)
     return w;
 }
 
+// Alignment the kernels' vector accesses need: 16 bytes for x, conv weights, conv windows,
+// outputs and the workspace; 4 bytes for g, beta and S.
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
 static bool overlap(const void *a, size_t na, const void *b, size_t nb)
 {
     if (!a || !b || na == 0 || nb == 0) return false;
@@ -80,8 +85,8 @@ static bool states_same(const gdn_state *a, const gdn_state *b)
 
 static gdn_status check_state(const gdn_desc &d, const gdn_state *s)
 {
-    if (!s || !s->S) return GDN_EINVAL;
-    if (d.conv_width > 0 && !s->conv) return GDN_EINVAL;
+    if (!s || !s->S || !aligned(s->S, 4)) return GDN_EINVAL;
+    if (d.conv_width > 0 && (!s->conv || !aligned(s->conv, 16))) return GDN_EINVAL;
     if (s->pos < 0) return GDN_EINVAL;
     if (s->tag != gdn_desc_tag(&d)) return GDN_EMISMATCH;
     return GDN_OK;
@@ -300,7 +305,8 @@ gdn_status gdn_prefill_chunked_events(const gdn_desc *d, const void *x, const vo
     if (mode != GDN_COMMIT && mode != GDN_FORK) return GDN_EINVAL;
     if (T < 0 || T > INT32_MAX) return GDN_EINVAL;
     if ((st = check_state(*d, in))) return st;
-    if (!out || !out->S || (d->conv_width > 0 && !out->conv)) return GDN_EINVAL;
+    if (!out || !out->S || !aligned(out->S, 4)) return GDN_EINVAL;
+    if (d->conv_width > 0 && (!out->conv || !aligned(out->conv, 16))) return GDN_EINVAL;
     int64_t n;
     if (mode == GDN_COMMIT) {
         if (in->pos % d->grid != 0) return GDN_EGRID;
@@ -313,9 +319,13 @@ gdn_status gdn_prefill_chunked_events(const gdn_desc *d, const void *x, const vo
     }
     if (n > 0) {
         if (!x || !g || !beta || !o || (d->conv_width > 0 && !conv_w)) return GDN_EINVAL;
+        if (!aligned(x, 16) || !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4) ||
+            (d->conv_width > 0 && !aligned(conv_w, 16)))
+            return GDN_EINVAL;
         const int64_t piece = max_rows_per_launch(*d);
         if (!ws || ws_bytes < workspace_bytes(*d, (std::min(n, piece) + kC - 1) / kC))
             return GDN_EWORKSPACE;
+        if (!aligned(ws, 16)) return GDN_EINVAL;
         const int64_t pos0 = in->pos;
         const uint64_t tag = in->tag;
         for (int64_t r0 = 0; r0 < n; r0 += piece) {
@@ -358,13 +368,17 @@ gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_
         if (cu_rows[b + 1] - cu_rows[b] > max_rows_per_launch(*d)) return GDN_ESHAPE;
     }
     if (!x || !g || !beta || !o || (d->conv_width > 0 && !conv_w)) return GDN_EINVAL;
+    if (!aligned(x, 16) || !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4) ||
+        (d->conv_width > 0 && !aligned(conv_w, 16)))
+        return GDN_EINVAL;
     for (int32_t b = 0; b < B; ++b) {
         if ((st = check_state(*d, init[b]))) return st;
         if (init[b]->pos % GDN_SUB_CHUNK != 0) return GDN_EGRID;
     }
     if (out) {
         for (int32_t b = 0; b < B; ++b) {
-            if (!out[b] || !out[b]->S || (d->conv_width > 0 && !out[b]->conv)) return GDN_EINVAL;
+            if (!out[b] || !out[b]->S || !aligned(out[b]->S, 4)) return GDN_EINVAL;
+            if (d->conv_width > 0 && (!out[b]->conv || !aligned(out[b]->conv, 16))) return GDN_EINVAL;
             for (int32_t j = 0; j < B; ++j)
                 if (states_overlap(*d, out[b], init[j])) return GDN_EALIAS;
             for (int32_t j = 0; j < b; ++j)
@@ -389,6 +403,7 @@ gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_
     const size_t s_bytes = gdn_state_S_bytes(d), c_bytes = align256(gdn_state_conv_bytes(d));
     if (!out) need += (size_t)std::min<int32_t>(B, kMaxSegPerLaunch) * (align256(s_bytes) + c_bytes);
     if (!ws || ws_bytes < need) return GDN_EWORKSPACE;
+    if (!aligned(ws, 16)) return GDN_EINVAL;
     if (!out) {
         // scratch final states, reused by every launch group (ordered on the stream)
         char *tail = (char *)ws + workspace_bytes(*d, subs);

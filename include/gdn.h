@@ -12,7 +12,7 @@
  *    checkpoints, one per turn's prompt end; on a differing prompt go back to the newest
  *    checkpoint at or below the first differing token, or start over.
  *  - PR "qwen3_5: run prompts that share prefixes once per prefix", section Purpose: a
- *    prefix state is the float32 recurrent state plus the last three conv inputs; each
+ *    prefix state holds the fp32 recurrent state and the three most recent conv inputs; each
  *    prefix is run up to its last multiple of 64 rows and the remainder runs with every
  *    later group or branch; each branch continues from the shared state; invalid requests
  *    are refused before any device work (section "Test Result").
@@ -24,11 +24,13 @@
  *    no device memory and keeps no pointer after a call returns.  Host pointers likewise.
  *  - Every argument is validated on the host first.  A negative return means nothing was
  *    enqueued and no state byte, position or tag changed.
+ *  - Device pointers must be aligned: 16 bytes for x, conv_w, o, conv windows and the
+ *    workspace, 4 bytes for g, beta and S (GDN_EINVAL otherwise).
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without synchronising.  GDN_EDEVICE reports a failed launch or copy; the
  *    outputs are then undefined.
  *  - The library holds no global mutable state; calls on different streams may overlap as
- *    long as they write disjoint memory.
+ *    long as they write disjoint memory (and use different workspaces).
  *
  * Layouts (row-major, innermost last):
  *   C   = 2*n_k_heads*d_k + n_v_heads*d_v conv channels, ordered q | k | v, each head's

@@ -103,6 +103,15 @@ def test_prefill_validation_refuses_before_device_work():
         (dict(sin=s, sout=s, conv_w=None), b.GDN_EINVAL),
         # overlapping but not identical output state in a commit
         (dict(sin=s, sout=_state(pos=512, S=FAKE + 64, conv=FAKE + (7 << 30))), b.GDN_EALIAS),
+        # misaligned device pointers
+        (dict(sin=s, sout=s, x=FAKE + 2), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, o=FAKE + 8), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, conv_w=FAKE + 4), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, g=FAKE + 2), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, beta=FAKE + 1), b.GDN_EINVAL),
+        (dict(sin=_state(pos=512, S=FAKE + 2), sout=_state(pos=512, S=FAKE + 2)), b.GDN_EINVAL),
+        (dict(sin=s, sout=_state(pos=512, S=FAKE + (15 << 30), conv=FAKE + (16 << 30) + 8)),
+         b.GDN_EINVAL),
     ]
     for kw, code in cases:
         sin, sout = kw.pop("sin"), kw.pop("sout")

@@ -149,3 +149,41 @@ def test_conv1d_state_step(b):
                                         synth.f64(win0))
     assert rel_l2(y.cpu().numpy(), y_ref) < 1e-6
     assert np.array_equal(synth.f64(window), w_ref)
+
+
+@pytest.mark.parametrize("shape", [synth.Shape(4, 16, 128, 128, 4), synth.Shape(2, 6, 64, 64, 4)],
+                         ids=["group4_d128", "group3_d64"])
+def test_gqa_groups_beyond_two(b, shape):
+    """Four or three value heads per key head: the prep kernel takes the value heads of a key
+    head two at a time, the last pass of an odd group with one head."""
+    d = _desc(b, shape)
+    inp = synth.layer_inputs(shape, 333, seed=8)
+    o, s1 = run_fork(b, d, to_dev(inp), new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, w_ref = oracle(d, inp)
+    _check_parity(o, s1.S, o_ref, S_ref)
+    assert np.array_equal(synth.f64(s1.conv), w_ref)
+
+
+def test_conv_silu(b):
+    """The conv followed by SiLU (the switch the descriptor carries)."""
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape, conv_silu=True)
+    inp = synth.layer_inputs(shape, 200, seed=9)
+    o, s1 = run_fork(b, d, to_dev(inp), new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, w_ref = oracle(d, inp)
+    _check_parity(o, s1.S, o_ref, S_ref)
+    assert np.array_equal(synth.f64(s1.conv), w_ref)
+
+
+def test_fp32_activations_layer(b):
+    """fp32 x, conv weights and window with fp32 outputs at the layer shape."""
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape, act=torch.float32, out=torch.float32)
+    inp = synth.layer_inputs(shape, 300, seed=10, act_dtype=torch.float32)
+    o, s1 = run_fork(b, d, to_dev(inp), new_state(b, d))
+    torch.cuda.synchronize()
+    o_ref, S_ref, w_ref = oracle(d, inp)
+    _check_parity(o, s1.S, o_ref, S_ref)
+    assert np.array_equal(synth.f64(s1.conv), w_ref)
