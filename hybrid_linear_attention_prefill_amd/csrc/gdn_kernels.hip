@@ -23,11 +23,14 @@
 //                  Tinv (blocked forward substitution in LDS, fp32) and the decayed mask M.
 //                  Everything it writes is independent of the state, so all sub-chunks run
 //                  in parallel.
-//   chain_kernel   grid (d_v tiles of 16, value heads, sequences): the serial walk over the
-//                  sub-chunks.  Columns of S evolve independently, so each workgroup owns
-//                  S[:, 16 columns] in MFMA accumulators (fp32) for the whole call, with an
-//                  fp16 copy in LDS as the MFMA operand.  It also convolves its own v columns.
-//   window_kernel  the new conv window = the last 3 rows of (window ++ x), copied bit for bit.
+//   chain_kernel   grid (d_v tiles of 16, value heads, sequences), 8 waves: the serial walk
+//                  over the sub-chunks.  Columns of S evolve independently, so each workgroup
+//                  owns S[:, 16 columns] in MFMA accumulators (fp32) for the whole call, with an
+//                  fp16 copy in LDS as the MFMA operand.  Four waves run the recurrence, four
+//                  compute the outputs, convolve the workgroup's v columns and stage the shared
+//                  tables.  It also writes the sequence's new conv window.
+//   window_kernel  the new conv window = the last 3 rows of (window ++ x), copied bit for bit
+//                  (the standalone conv step).
 //
 // Precision: every MFMA takes fp16 operands (v_mfma_f32_16x16x32_f16, same peak as bf16 on
 // gfx950) with fp32 accumulation; all operands are bounded (unit-norm q/k, decays <= 1,
@@ -94,17 +97,32 @@ __device__ __forceinline__ f32x4 mfma16(half8 a, half8 b, f32x4 c)
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 
-// A fragment of K^T for the 16x16x32 MFMA read straight from row-major K in LDS:
+// Half offset of K[t][c] in a K tile: the 16-byte chunk c / 8 of row t is XORed with a
+// permutation of the low four bits of t.  The 16 rows that a 16-lane group writes then hit
+// distinct chunks, and so do the 8 rows x 2 chunks that 32 lanes of a transposed read
+// (ds_read_b64_tr_b16) touch: both are free of bank conflicts.
+__device__ __forceinline__ int k_off(int t, int c)
+{
+    const int f = ((t >> 3) & 1) * 8 + ((t >> 1) & 1) * 4 + (t & 1) * 2 + ((t >> 2) & 1);
+    return t * 128 + 8 * ((c >> 3) ^ f) + (c & 7);
+}
+
+// Half offset of element p of row `col` in a [16][128] tile (S^T, R^T, D^T): the 8-byte chunk
+// p / 4 is XORed with 2 col.  A 16-byte B-fragment read (chunks 2m, 2m+1) stays contiguous,
+// and the 16 columns read by a lane group hit distinct chunk pairs.
+__device__ __forceinline__ int c_off(int col, int p) { return col * 128 + 4 * ((p >> 2) ^ (2 * col)) + (p & 3); }
+
+// A fragment of K^T for the 16x16x32 MFMA read straight from the K tile in LDS (k_off):
 // lane (m, kg) of the result holds K[r0 + 8 kg + e][c0 + m], e = 0..7.  ds_read_b64_tr_b16
 // hands lane i of each 16-lane group element i % 4 of the 4-element reads of lanes
 // 4 e + i / 4, so lane j reads K[row0 + j / 4][c0 + 4 (j % 4) .. + 3] (rows row0 .. row0 + 3).
-__device__ __forceinline__ half8 ktrans_frag(const _Float16 *K, int stride, int r0, int c0, int lane)
+__device__ __forceinline__ half8 ktrans_frag(const _Float16 *K, int r0, int c0, int lane)
 {
     const int j = lane % 16, kg = lane / 16;
-    const _Float16 *p0 = K + (r0 + 8 * kg + j / 4) * stride + c0 + 4 * (j % 4);
+    const int r = r0 + 8 * kg + j / 4, c = c0 + 4 * (j % 4);
     typedef __attribute__((address_space(3))) short4_t lds_short4;
-    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(p0));
-    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(p0 + 4 * stride));
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(K + k_off(r, c)));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(K + k_off(r + 4, c)));
     return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0, 1,
                                    2, 3, 4, 5, 6, 7);
 }
@@ -498,24 +516,60 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__r
 #undef BLK
 }
 
-// Per-lane register set of one sub-chunk's chain inputs.  Compute wave w handles rows
-// 16w .. 16w+15: its MFMA A fragments of K, Q, Tinv and M come straight into registers.  Each
-// thread also carries LP 16-byte chunks bound for LDS: first the raw v rows of this
-// workgroup's 16 columns (3 halo rows + 64), then the 1 KB factor table.
+// ------------------------------------------------------------------------------------------
+// chain_kernel: the serial walk of one (d_v tile, value head, sequence) over its sub-chunks.
+//
+// Eight waves, two per SIMD, in two roles that meet at the same three barriers per step:
+//   state waves 0-3  the recurrence.  Wave c computes rows 16c .. 16c+15 of X = K S and of
+//                    D = Tinv R, and d_k rows 32c .. 32c+31 (D = 128) of the state tile, which
+//                    it keeps in fp32 registers for the whole call.
+//   output waves 4-7 everything off the recurrence: P = Q S, O = scale (gamma P + M D) and
+//                    its store, and beta * conv(v) of the next sub-chunk.
+// Every wave loads the fragments and gate factors it uses straight into its own registers,
+// two sub-chunks ahead; LDS carries what one wave computes for another (S^T, R^T, D^T,
+// beta conv(v)), K for its transposed reads, and the raw v rows of the conv.  The LDS unit
+// and the vector-memory queue are the scarce resources of a step, so:
+//  - every LDS tile is laid out so that its reads and writes are free of bank conflicts
+//    (rows of 256 bytes whose 8- or 16-byte chunks are XOR-swizzled by row; see k_off and
+//    c_off), which halves the cycles the unit spends per instruction;
+//  - the raw v rows come in with one 16-byte load per output thread and pass through LDS, not
+//    as seven 2-byte loads per lane;
+//  - the three phases are balanced in LDS instructions:
+//   phase 1  state: X = K S (S from LDS), R = beta v - beta gamma X -> LDS
+//            output: O of the previous sub-chunk (its D still in LDS), stored; the raw v
+//                   rows and factors of the next sub-chunk -> LDS
+//   phase 2  state: D = Tinv R -> LDS (as is, and times exp(G_n - G)); K rows of the next
+//                   sub-chunk -> LDS
+//            output: P = Q S (S read here rather than in phase 1), times gamma
+//   phase 3  state: S' = gamma_n S + K^T (exp(G_n - G) D); its fp16 copy -> LDS
+//            output: beta * conv(v) of the next sub-chunk -> LDS
+// ------------------------------------------------------------------------------------------
+
+// What a state wave loads for one sub-chunk: its K (A operand of X) and Tinv (A operand of D)
+// fragments.
+template <int D>
+struct StateRegs {
+    static constexpr int KB = D / 32;  // 32-wide K steps over d_k
+    half8 kf[KB], tf[2];
+};
+
+// What an output wave loads for one sub-chunk: Q and M fragments, and LP 16-byte chunks bound
+// for LDS: the raw v rows of this workgroup's 16 columns (3 halo rows + 64), then the 1 KB
+// factor table (every wave reads factors of many rows, so one copy in LDS serves all).
 template <int D, typename Act>
-struct StepRegs {
-    static constexpr int KB = D / 32;                  // 32-wide K steps over d_k
+struct OutRegs {
+    static constexpr int KB = D / 32;
     static constexpr int EPC = 16 / (int)sizeof(Act);
     static constexpr int VCR = 16 / EPC;               // chunks per v row (16 values)
     static constexpr int VC = (kC + 3) * VCR;          // v chunks
     static constexpr int NLD = VC + 64;                // + factor table chunks
-    static constexpr int LP = (NLD + 255) / 256;       // LDS-bound chunks per thread
-    half8 kf[KB], qf[KB], tf[2], mf[2];
+    static constexpr int LP = (NLD + 255) / 256;       // chunks per output thread
+    half8 qf[KB], mf[2];
     u32x4 ld[LP];
 };
 
 struct ChainArgs {
-    int sub0, seg_n, kh, h, Hk, Hv, C, vch, conv_on, c0, wave, col, kg, tid;
+    int sub0, seg_n, kh, h, Hk, Hv, C, vch, c0, wave, col, kg, ot;
     int64_t seg_row0;
     // Buffer resources: their range checks return 0 for reads outside the sequence (rows past
     // its end or before its start) and drop writes outside it, so loads and stores need no
@@ -526,96 +580,127 @@ struct ChainArgs {
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-// Prefetch of one sub-chunk's chain inputs into register set R, in parts so that a step
-// spreads its loads over its length (one batch of fourteen 1 KB loads from every wave at once
-// stalls the waves at issue): PART 0 the raw v rows and factors (consumed one step later), 1
-// the K fragments, 2 the Q fragments, 3 the Tinv and M fragments; -1 all of them.
-template <int D, typename Act, int PART>
-__device__ __forceinline__ void step_issue(StepRegs<D, Act> &R, const ChainArgs &a, int cl,
-                                           const Workspace &ws)
+// State-wave prefetch of sub-chunk `cl`: PART 1 the K fragments, 2 the Tinv fragments.
+template <int D, int PART>
+__device__ __forceinline__ void state_issue(StateRegs<D> &R, const ChainArgs &a, int cl,
+                                            const Workspace &ws)
 {
-    using SR = StepRegs<D, Act>;
-    const int sub = a.sub0 + cl, rb = cl * kC;
+    using SR = StateRegs<D>;
+    const int sub = a.sub0 + cl;
     const int lane = 16 * a.kg + a.col;
-    if constexpr (PART == 0 || PART == -1) {
-        const u32x4 *Fg = (const u32x4 *)(ws.Fac + ((int64_t)sub * a.Hv + a.h) * 4 * kC);
-#pragma unroll
-        for (int i = 0; i < SR::LP; ++i) {
-            const int idx = a.tid + 256 * i;
-            if (idx < SR::VC) {
-                const int vr = idx / SR::VCR, cc = (idx % SR::VCR) * SR::EPC;
-                const int sr = rb + vr - 3;  // sequence-local row (rows before 0: the window, added apart)
-                R.ld[i] = __builtin_amdgcn_raw_buffer_load_b128(a.rx, (sr * a.C + a.vch + cc) * (int)sizeof(Act), 0, 0);
-            } else {
-                R.ld[i] = Fg[min(idx - SR::VC, 63)];
-            }
-        }
-    }
-    if constexpr (PART == 1 || PART == -1) {
+    if constexpr (PART == 1) {
         const half8 *Kg = (const half8 *)(ws.Kh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
 #pragma unroll
         for (int kb = 0; kb < SR::KB; ++kb) R.kf[kb] = Kg[kb * 64];
-    }
-    if constexpr (PART == 2 || PART == -1) {
-        const half8 *Qg = (const half8 *)(ws.Qh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * SR::KB * 64 + lane;
-#pragma unroll
-        for (int kb = 0; kb < SR::KB; ++kb) R.qf[kb] = Qg[kb * 64];
-    }
-    if constexpr (PART == 3 || PART == -1) {
+    } else {
         const half8 *Tg = (const half8 *)(ws.Tm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
-        const half8 *Mg = (const half8 *)(ws.Mm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
-        const half8 z = {};
         R.tf[0] = Tg[64 * tri_frag(a.wave, 0)];
+        R.tf[1] = (a.wave >= 2) ? Tg[64 * tri_frag(a.wave, 1)] : half8{};  // wave-uniform
+    }
+}
+
+// Output-wave prefetch of sub-chunk `cl`: PART 1 the Q fragments, 2 the M fragments, 3 the raw
+// v rows and the factor table.
+template <int D, typename Act, int PART>
+__device__ __forceinline__ void out_issue(OutRegs<D, Act> &R, const ChainArgs &a, int cl,
+                                          const Workspace &ws)
+{
+    using OR = OutRegs<D, Act>;
+    const int sub = a.sub0 + cl;
+    const int lane = 16 * a.kg + a.col;
+    if constexpr (PART == 1) {
+        const half8 *Qg = (const half8 *)(ws.Qh + ((int64_t)sub * a.Hk + a.kh) * kC * D) + a.wave * OR::KB * 64 + lane;
+#pragma unroll
+        for (int kb = 0; kb < OR::KB; ++kb) R.qf[kb] = Qg[kb * 64];
+    } else if constexpr (PART == 2) {
+        const half8 *Mg = (const half8 *)(ws.Mm + ((int64_t)sub * a.Hv + a.h) * kPackedTri) + lane;
         R.mf[0] = Mg[64 * tri_frag(a.wave, 0)];
-        if (a.wave >= 2) {  // wave-uniform
-            R.tf[1] = Tg[64 * tri_frag(a.wave, 1)];
-            R.mf[1] = Mg[64 * tri_frag(a.wave, 1)];
-        } else {
-            R.tf[1] = z;
-            R.mf[1] = z;
+        R.mf[1] = (a.wave >= 2) ? Mg[64 * tri_frag(a.wave, 1)] : half8{};  // wave-uniform
+    } else {
+        const u32x4 *Fg = (const u32x4 *)(ws.Fac + ((int64_t)sub * a.Hv + a.h) * 4 * kC);
+#pragma unroll
+        for (int i = 0; i < OR::LP; ++i) {
+            const int idx = a.ot + 256 * i;
+            if (idx < OR::VC) {
+                const int vr = idx / OR::VCR, cc = (idx % OR::VCR) * OR::EPC;
+                const int sr = cl * kC + vr - 3;  // sequence-local row (rows before 0: the window, added apart)
+                R.ld[i] = __builtin_amdgcn_raw_buffer_load_b128(a.rx, (sr * a.C + a.vch + cc) * (int)sizeof(Act), 0, 0);
+            } else {
+                R.ld[i] = Fg[min(idx - OR::VC, 63)];
+            }
         }
     }
 }
 
-// LDS of the chain kernel: K of the current sub-chunk (for the transposed reads of the state
-// update), the raw v rows, the factor tables (double-buffered), S^T as the fp16 MFMA operand,
-// and the transposed 64 x 16 tiles.
+// LDS of the chain kernel.  Every fp16 tile has rows of 128 halves (256 bytes, all 64 banks).
 template <int D, typename Act>
 struct ChainLds {
-    static constexpr int HS = D + 8, TS = kC + 8, ST = D + 8;
-    _Float16 k16[kC * HS];
-    _Float16 s16t[16 * ST];
-    _Float16 rt[16 * TS], dt[16 * TS], ddt[16 * TS];
-    u32x4 xvr[StepRegs<D, Act>::VC];
-    float fac[2][4 * kC];  // per row: beta, beta*gamma, gamma, exp(G_n - G)
+    static constexpr int RW = 128, BS = kC + 8;
+    _Float16 k16[2][kC * RW];              // K rows of this step (transposed reads), double-buffered
+    _Float16 s16t[16 * RW];                // S^T, fp16: the B operand of X and P
+    _Float16 rt[16 * RW], dt[16 * RW], ddt[16 * RW];  // R^T, D^T, (exp(G_n - G) D)^T
+    float bv[16 * BS];                     // beta * conv(v) of the next step, [column][row]
+    u32x4 xvr[OutRegs<D, Act>::VC];        // raw v rows of the next step (3 halo rows + 64)
+    float fac[2][4 * kC];                  // per row: beta, beta*gamma, gamma, exp(G_n - G)
 };
 
+
+// Output wave: the raw v rows and the factor table of register set R into LDS (factor buffer
+// `buf`).  The halo rows of a sequence's first sub-chunk come from the conv window (`win`
+// non-null): the x loads returned 0 there.
 template <int D, typename Act>
-__device__ __forceinline__ void put_ld(ChainLds<D, Act> &L, const StepRegs<D, Act> &R, int tid, int buf)
+__device__ __forceinline__ void put_ld(ChainLds<D, Act> &L, const OutRegs<D, Act> &R, const ChainArgs &a,
+                                       int buf, const Act *win)
 {
-    using SR = StepRegs<D, Act>;
+    using OR = OutRegs<D, Act>;
 #pragma unroll
-    for (int i = 0; i < SR::LP; ++i) {
-        const int idx = tid + 256 * i;
-        if (idx < SR::VC)
-            L.xvr[idx] = R.ld[i];
-        else if (idx < SR::NLD)
-            ((u32x4 *)L.fac[buf])[idx - SR::VC] = R.ld[i];
+    for (int i = 0; i < OR::LP; ++i) {
+        const int idx = a.ot + 256 * i;
+        u32x4 v = R.ld[i];
+        if (idx < OR::VC) {
+            if (win != nullptr && idx < 3 * OR::VCR) {
+                const int vr = idx / OR::VCR, cc = (idx % OR::VCR) * OR::EPC;
+                v = v | *(const u32x4 *)(win + (int64_t)vr * a.C + a.vch + cc);
+            }
+            L.xvr[idx] = v;
+        } else if (idx < OR::NLD) {
+            ((u32x4 *)L.fac[buf])[idx - OR::VC] = v;
+        }
     }
 }
 
-// One step of the chain over sub-chunk `cl` with register set K (step index modulo 3).
-template <int K, int D, typename Act, typename Out, bool SILU>
-__device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act> (&R)[3],
-                                           const ChainArgs &a, int cl, int nsub, f32x4 (&S)[D / 64],
-                                           float w0, float w1, float w2, float w3, float scale,
-                                           const Workspace &ws)
+// Output wave: beta * conv(v) of rows 16 wave + 4 kg .. +3, column col, from the raw rows in
+// LDS and beta of factor buffer `buf`, into L.bv.
+template <int D, typename Act, bool SILU>
+__device__ __forceinline__ void conv_bv(ChainLds<D, Act> &L, const ChainArgs &a, int buf, float w0,
+                                        float w1, float w2, float w3)
 {
     using CL = ChainLds<D, Act>;
-    using SR = StepRegs<D, Act>;
-    constexpr int HS = CL::HS, TS = CL::TS, ST = CL::ST;
+    const int r0 = 16 * a.wave + 4 * a.kg;
+    const Act *vrows = (const Act *)L.xvr;
+    float vr[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * 16 + a.col]);
+    const f32x4 fb = *(const f32x4 *)(L.fac[buf] + r0);
+    f32x4 bvv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float v = w0 * vr[i] + w1 * vr[i + 1] + w2 * vr[i + 2] + w3 * vr[i + 3];
+        if constexpr (SILU) v = v / (1.f + expf(-v));
+        bvv[i] = fb[i] * v;
+    }
+    *(f32x4 *)(L.bv + a.col * CL::BS + r0) = bvv;
+}
+
+// One step of a state wave over sub-chunk `cl` with register set K (step index modulo 3).
+template <int K, int D, typename Act>
+__device__ __forceinline__ void state_step(ChainLds<D, Act> &L, StateRegs<D> (&R)[3], const ChainArgs &a,
+                                           int cl, int nsub, f32x4 (&S)[D / 64], const Workspace &ws)
+{
+    using CL = ChainLds<D, Act>;
+    using SR = StateRegs<D>;
     constexpr int TPW = D / 64;  // d_k tiles per wave
-    StepRegs<D, Act> &C = R[K];
+    const StateRegs<D> &C = R[K];
     const int wave = a.wave, col = a.col, kg = a.kg, lane = a.kg * 16 + a.col;
     const int r0 = 16 * wave + 4 * kg;
     // Tinv and M fragments order their 32-wide K steps as (4 rows of tile 2kb, 4 rows of tile
@@ -624,49 +709,36 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
     const int pr0 = 32 * (wave / 2) + 8 * kg + 4 * (wave % 2);
     const float *F = L.fac[cl & 1];
     const int cn = min(cl + 2, nsub - 1);  // the sub-chunk whose inputs this step prefetches
-    step_issue<D, Act, 1>(R[(K + 2) % 3], a, cn, ws);
+    state_issue<D, 1>(R[(K + 2) % 3], a, cn, ws);
 
-    // X = K S and P = Q S for row tile `wave`
-    f32x4 X = {0.f, 0.f, 0.f, 0.f}, P = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < SR::KB; ++kb) {
-        const half8 bS = *(const half8 *)(L.s16t + col * ST + 32 * kb + 8 * kg);
-        X = mfma16(C.kf[kb], bS, X);
-        P = mfma16(bS, C.qf[kb], P);  // P transposed: this lane's row, four adjacent columns
-    }
-    // R = beta V - beta gamma X; the state part of O is gamma P
-    f32x4 Ob;
-    {
-        const Act *vrows = (const Act *)L.xvr;
-        const f32x4 fb = *(const f32x4 *)(F + r0), fbg = *(const f32x4 *)(F + kC + r0);
-        const float fg = F[2 * kC + 16 * wave + col];  // gamma of row 16 wave + col
-        float vr[7];
-#pragma unroll
-        for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * 16 + col]);
-        half4 rv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float v = w0 * vr[i] + w1 * vr[i + 1] + w2 * vr[i + 2] + w3 * vr[i + 3];
-            if constexpr (SILU) v = v / (1.f + expf(-v));
-            rv[i] = (_Float16)(fb[i] * v - fbg[i] * X[i]);
-            Ob[i] = fg * P[i];
-        }
-        *(half4 *)(L.rt + col * TS + pr0) = rv;
-    }
-    step_issue<D, Act, 0>(R[(K + 2) % 3], a, cn, ws);
-    __syncthreads();  // #1: rt complete; xvr, K and the other factor buffer are free
-
-    // this step's K rows into LDS for the state update; next step's v rows and factors
+    // phase 1: X = K S for row tile `wave`; R = beta v - beta gamma X
+    f32x4 X = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < SR::KB; ++kb)
-        *(half8 *)(L.k16 + (16 * wave + col) * HS + 32 * kb + 8 * kg) = C.kf[kb];
-    put_ld<D, Act>(L, R[(K + 1) % 3], a.tid, (cl + 1) & 1);
+        X = mfma16(C.kf[kb], *(const half8 *)(L.s16t + c_off(col, 32 * kb + 8 * kg)), X);
+    {
+        const f32x4 bv = *(const f32x4 *)(L.bv + col * CL::BS + r0);
+        const f32x4 fbg = *(const f32x4 *)(F + kC + r0);
+        half4 rv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv[i] = (_Float16)(bv[i] - fbg[i] * X[i]);
+        *(half4 *)(L.rt + c_off(col, pr0)) = rv;
+    }
+    __syncthreads();  // #1: rt complete
 
-    // D = Tinv R (fragments above the diagonal are zero)
+    // phase 2: D = Tinv R (fragments above the diagonal are zero); this step's K rows for the
+    // transposed reads of phase 3
+    state_issue<D, 2>(R[(K + 2) % 3], a, cn, ws);
     f32x4 Dl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-        Dl = mfma16(C.tf[kb], *(const half8 *)(L.rt + col * TS + 32 * kb + 8 * kg), Dl);
+        Dl = mfma16(C.tf[kb], *(const half8 *)(L.rt + c_off(col, 32 * kb + 8 * kg)), Dl);
+    {
+        _Float16 *kn = L.k16[cl & 1];
+#pragma unroll
+        for (int kb = 0; kb < SR::KB; ++kb)
+            *(half8 *)(kn + k_off(16 * wave + col, 32 * kb + 8 * kg)) = C.kf[kb];
+    }
     {
         const f32x4 fd = *(const f32x4 *)(F + 3 * kC + r0);
         half4 dv, ddv;
@@ -675,62 +747,96 @@ __device__ __forceinline__ void chain_step(ChainLds<D, Act> &L, StepRegs<D, Act>
             dv[i] = (_Float16)Dl[i];
             ddv[i] = (_Float16)(fd[i] * Dl[i]);
         }
-        *(half4 *)(L.dt + col * TS + pr0) = dv;
-        *(half4 *)(L.ddt + col * TS + r0) = ddv;
+        *(half4 *)(L.dt + c_off(col, pr0)) = dv;
+        *(half4 *)(L.ddt + c_off(col, r0)) = ddv;
     }
-    step_issue<D, Act, 2>(R[(K + 2) % 3], a, cn, ws);
-    __syncthreads();  // #2: dt, ddt and K complete
+    __syncthreads();  // #2: dt, ddt and the K rows complete
 
-    // S' = gamma_n S + K^T (exp(G_n - G) D)
+    // phase 3: S' = gamma_n S + K^T (exp(G_n - G) D)
     {
-        const float gn = F[3 * kC - 1];
+        const _Float16 *kc = L.k16[cl & 1];
         half8 bd[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) bd[kb] = *(const half8 *)(L.ddt + col * TS + 32 * kb + 8 * kg);
+        for (int kb = 0; kb < 2; ++kb) bd[kb] = *(const half8 *)(L.ddt + c_off(col, 32 * kb + 8 * kg));
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int kt = wave * TPW + t;
-            f32x4 acc = S[t] * gn;
+            f32x4 acc = S[t] * F[3 * kC - 1];  // gamma_n: gamma of the last row
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-                acc = mfma16(ktrans_frag(L.k16, HS, 32 * kb, 16 * kt, lane), bd[kb], acc);
+                acc = mfma16(ktrans_frag(kc, 32 * kb, 16 * kt, lane), bd[kb], acc);
             S[t] = acc;
             half4 sv;
 #pragma unroll
             for (int i = 0; i < 4; ++i) sv[i] = (_Float16)acc[i];
-            *(half4 *)(L.s16t + col * ST + 16 * kt + 4 * kg) = sv;
+            *(half4 *)(L.s16t + c_off(col, 16 * kt + 4 * kg)) = sv;
         }
     }
-    // O = scale (gamma Q S + M D)
-    {
-        // transposed product (D^T M^T): this lane gets row 16 wave + col, columns 4 kg .. +3
-        f32x4 Oa = Ob;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            Oa = mfma16(*(const half8 *)(L.dt + col * TS + 32 * kb + 8 * kg), C.mf[kb], Oa);
-        const int obase = ((cl * kC + 16 * wave + col) * a.Hv + a.h) * D + a.c0 + 4 * kg;
-        store_out4<Out>(a.ro, obase, Oa * scale);
-    }
-    step_issue<D, Act, 3>(R[(K + 2) % 3], a, cn, ws);
     __syncthreads();  // #3: s16t complete for the next step
 }
 
-// ------------------------------------------------------------------------------------------
-// chain_kernel: the serial walk of one (d_v tile, value head, sequence) over its sub-chunks.
-// Four waves; wave w owns rows 16w .. 16w+15 of every 64-row product and d_k rows
-// 32w .. 32w+31 (D = 128) of the state tile.  Each wave loads its own MFMA fragments straight
-// into registers two sub-chunks ahead; K (needed transposed by the other waves), the raw v rows
-// and the factor table pass through LDS.  Three barriers per step.
-// ------------------------------------------------------------------------------------------
+// Output wave: O of sub-chunk `cl` = scale (gamma P + M D), transposed (D^T M^T) like P, from
+// Ob = gamma P, the M fragments mf and D^T in LDS; this lane stores row 16 wave + col,
+// columns 4 kg .. +3.
+template <int D, typename Act, typename Out>
+__device__ __forceinline__ void out_store(const ChainLds<D, Act> &L, const ChainArgs &a, int cl, f32x4 Ob,
+                                          const half8 (&mf)[2], float scale)
+{
+    f32x4 Oa = Ob;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+        Oa = mfma16(*(const half8 *)(L.dt + c_off(a.col, 32 * kb + 8 * a.kg)), mf[kb], Oa);
+    const int obase = ((cl * kC + 16 * a.wave + a.col) * a.Hv + a.h) * D + a.c0 + 4 * a.kg;
+    store_out4<Out>(a.ro, obase, Oa * scale);
+}
+
+// One step of an output wave over sub-chunk `cl` with register set K.  Ob and mcur carry gamma P
+// and the M fragments of the previous sub-chunk into this step's phase 1.  The raw v rows,
+// which come from HBM, are loaded three steps ahead: set K holds those of sub-chunk cl + 3
+// (its previous rows, of sub-chunk cl, went to LDS one step ago).
+template <int K, int D, typename Act, typename Out, bool SILU>
+__device__ __forceinline__ void out_step(ChainLds<D, Act> &L, OutRegs<D, Act> (&R)[3], const ChainArgs &a,
+                                         int cl, int nsub, f32x4 &Ob, half8 (&mcur)[2], float w0,
+                                         float w1, float w2, float w3, float scale,
+                                         const Workspace &ws)
+{
+    using OR = OutRegs<D, Act>;
+    const OutRegs<D, Act> &C = R[K];
+    const int col = a.col, kg = a.kg;
+    const int cn = min(cl + 2, nsub - 1);
+
+    // phase 1: O of the previous sub-chunk (its D^T is in LDS until this step's phase 2); the
+    // next sub-chunk's raw v rows and factors
+    if (cl > 0) out_store<D, Act, Out>(L, a, cl - 1, Ob, mcur, scale);
+    put_ld<D, Act>(L, R[(K + 1) % 3], a, (cl + 1) & 1, nullptr);
+    out_issue<D, Act, 3>(R[K], a, min(cl + 3, nsub - 1), ws);
+    __syncthreads();  // #1
+
+    // phase 2: P = Q S, transposed (D^T of S^T Q^T): this lane's row 16 wave + col, columns
+    // 4 kg .. +3; the state part of O is gamma P
+    f32x4 P = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < OR::KB; ++kb)
+        P = mfma16(*(const half8 *)(L.s16t + c_off(col, 32 * kb + 8 * kg)), C.qf[kb], P);
+    Ob = P * L.fac[cl & 1][2 * kC + 16 * a.wave + col];
+    mcur[0] = C.mf[0];
+    mcur[1] = C.mf[1];
+    out_issue<D, Act, 2>(R[(K + 2) % 3], a, cn, ws);
+    __syncthreads();  // #2: dt complete
+
+    // phase 3: beta * conv(v) of the next step
+    if (cl + 1 < nsub) conv_bv<D, Act, SILU>(L, a, (cl + 1) & 1, w0, w1, w2, w3);
+    out_issue<D, Act, 1>(R[(K + 2) % 3], a, cn, ws);
+    __syncthreads();  // #3: bv complete for the next step
+}
+
 template <int D, typename Act, typename Out, bool SILU>
-__global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__restrict__ x,
+__global__ __launch_bounds__(512) void chain_kernel(SegArgs sa, const Act *__restrict__ x,
                                                     const Act *__restrict__ conv_w, int conv_on,
                                                     int Hk, int Hv, float scale, Workspace ws,
                                                     Out *__restrict__ o)
 {
     using CL = ChainLds<D, Act>;
-    using SR = StepRegs<D, Act>;
-    constexpr int ST = CL::ST;
     constexpr int TPW = D / 64;
     __shared__ __attribute__((aligned(16))) CL L;
 
@@ -740,6 +846,7 @@ __global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__res
     const int NTILE = D / kTileV, n_units = Hv * NTILE, id = blockIdx.x;
     const int unit = (n_units % 8 == 0) ? (id % 8) * (n_units / 8) + id / 8 : id;
     const int tile = unit % NTILE, h = unit / NTILE, s = blockIdx.y;
+    const bool state_role = threadIdx.x < 256;  // waves 0-3; waves 4-7 are output waves
     ChainArgs a;
     a.seg_row0 = sa.seg[s].row0;
     a.seg_n = sa.seg[s].n;
@@ -751,9 +858,8 @@ __global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__res
     a.C = 2 * Hk * D + Hv * D;
     a.c0 = tile * 16;
     a.vch = 2 * Hk * D + h * D + a.c0;
-    a.conv_on = conv_on;
-    a.tid = threadIdx.x;
-    a.wave = threadIdx.x >> 6;
+    a.ot = threadIdx.x & 255;
+    a.wave = (threadIdx.x >> 6) & 3;
     a.col = threadIdx.x % 16;
     a.kg = (threadIdx.x & 63) / 16;
     const Act *win = (const Act *)sa.seg[s].win_in;
@@ -766,58 +872,84 @@ __global__ __launch_bounds__(256) void chain_kernel(SegArgs sa, const Act *__res
     a.ro = __builtin_amdgcn_make_buffer_rsrc((void *)(o + a.seg_row0 * Hv * D), 0,
                                              a.seg_n * Hv * D * (int)sizeof(Out), kRsrcWord3);
 
-    float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f;
-    if (conv_on) {
-        w0 = to_f32(conv_w[(a.vch + col) * 4 + 0]);
-        w1 = to_f32(conv_w[(a.vch + col) * 4 + 1]);
-        w2 = to_f32(conv_w[(a.vch + col) * 4 + 2]);
-        w3 = to_f32(conv_w[(a.vch + col) * 4 + 3]);
-    }
-    StepRegs<D, Act> R[3];
-    if (nsub > 0) {
-        step_issue<D, Act, -1>(R[0], a, 0, ws);
-        step_issue<D, Act, -1>(R[1], a, min(1, nsub - 1), ws);
-    }
-    f32x4 S[TPW];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int kt = wave * TPW + t;
-        half4 sv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = 16 * kt + 4 * kg + i;
-            S[t][i] = S_in[((int64_t)h * D + k) * D + a.c0 + col];
-            sv[i] = (_Float16)S[t][i];
+    if (state_role) {
+        StateRegs<D> R[3];
+        if (nsub > 0) {
+            state_issue<D, 1>(R[0], a, 0, ws);
+            state_issue<D, 2>(R[0], a, 0, ws);
+            state_issue<D, 1>(R[1], a, min(1, nsub - 1), ws);
+            state_issue<D, 2>(R[1], a, min(1, nsub - 1), ws);
         }
-        *(half4 *)(L.s16t + col * ST + 16 * kt + 4 * kg) = sv;
-    }
-    if (nsub > 0) put_ld<D, Act>(L, R[0], a.tid, 0);
-    __syncthreads();
-    // the 3 halo rows of the first sub-chunk come from the window (the x loads gave 0 there)
-    if (conv_on && nsub > 0 && a.tid < 3 * SR::VCR) {
-        const int vr = a.tid / SR::VCR, cc = (a.tid % SR::VCR) * SR::EPC;
-        L.xvr[a.tid] = L.xvr[a.tid] | *(const u32x4 *)(win + (int64_t)vr * a.C + a.vch + cc);
-    }
-    __syncthreads();
-    // Whole triples of steps first, with no exits inside: every load issued in the loop is
-    // then consumed on every path, and the compiler's waits stay two steps behind the loads.
-    int cl = 0;
-    for (; cl + 3 <= nsub; cl += 3) {
-        chain_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, S, w0, w1, w2, w3, scale, ws);
-        chain_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, S, w0, w1, w2, w3, scale, ws);
-        chain_step<2, D, Act, Out, SILU>(L, R, a, cl + 2, nsub, S, w0, w1, w2, w3, scale, ws);
-    }
-    if (cl < nsub) chain_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, S, w0, w1, w2, w3, scale, ws);
-    if (cl + 1 < nsub) chain_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, S, w0, w1, w2, w3, scale, ws);
+        f32x4 S[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-        const int kt = wave * TPW + t;
+        for (int t = 0; t < TPW; ++t) {
+            const int kt = wave * TPW + t;
+            half4 sv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int k = 16 * kt + 4 * kg + i;
-            S_out[((int64_t)h * D + k) * D + a.c0 + col] = S[t][i];
+            for (int i = 0; i < 4; ++i) {
+                const int k = 16 * kt + 4 * kg + i;
+                S[t][i] = S_in[((int64_t)h * D + k) * D + a.c0 + col];
+                sv[i] = (_Float16)S[t][i];
+            }
+            *(half4 *)(L.s16t + c_off(col, 16 * kt + 4 * kg)) = sv;
         }
+        __syncthreads();  // prologue #1
+        __syncthreads();  // prologue #2
+        // Whole triples of steps first, with no exits inside: every load issued in the loop is
+        // then consumed on every path, and the compiler's waits stay behind the loads.
+        int cl = 0;
+        for (; cl + 3 <= nsub; cl += 3) {
+            state_step<0, D, Act>(L, R, a, cl, nsub, S, ws);
+            state_step<1, D, Act>(L, R, a, cl + 1, nsub, S, ws);
+            state_step<2, D, Act>(L, R, a, cl + 2, nsub, S, ws);
+        }
+        if (cl < nsub) state_step<0, D, Act>(L, R, a, cl, nsub, S, ws);
+        if (cl + 1 < nsub) state_step<1, D, Act>(L, R, a, cl + 1, nsub, S, ws);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int kt = wave * TPW + t;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = 16 * kt + 4 * kg + i;
+                S_out[((int64_t)h * D + k) * D + a.c0 + col] = S[t][i];
+            }
+        }
+    } else {
+        float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 1.f;
+        if (conv_on) {
+            w0 = to_f32(conv_w[(a.vch + col) * 4 + 0]);
+            w1 = to_f32(conv_w[(a.vch + col) * 4 + 1]);
+            w2 = to_f32(conv_w[(a.vch + col) * 4 + 2]);
+            w3 = to_f32(conv_w[(a.vch + col) * 4 + 3]);
+        }
+        OutRegs<D, Act> R[3];
+        f32x4 Ob = {0.f, 0.f, 0.f, 0.f};
+        half8 mcur[2] = {half8{}, half8{}};
+        if (nsub > 0) {
+            out_issue<D, Act, 3>(R[0], a, 0, ws);
+            out_issue<D, Act, 3>(R[1], a, min(1, nsub - 1), ws);
+            out_issue<D, Act, 3>(R[2], a, min(2, nsub - 1), ws);
+            out_issue<D, Act, 1>(R[0], a, 0, ws);
+            out_issue<D, Act, 2>(R[0], a, 0, ws);
+            out_issue<D, Act, 1>(R[1], a, min(1, nsub - 1), ws);
+            out_issue<D, Act, 2>(R[1], a, min(1, nsub - 1), ws);
+            put_ld<D, Act>(L, R[0], a, 0, conv_on ? win : nullptr);
+        }
+        __syncthreads();  // prologue #1: raw v rows and factors of step 0 in LDS
+        if (nsub > 0) conv_bv<D, Act, SILU>(L, a, 0, w0, w1, w2, w3);
+        __syncthreads();  // prologue #2: bv of step 0 in LDS
+        int cl = 0;
+        for (; cl + 3 <= nsub; cl += 3) {
+            out_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+            out_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+            out_step<2, D, Act, Out, SILU>(L, R, a, cl + 2, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+        }
+        if (cl < nsub) out_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+        if (cl + 1 < nsub) out_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+        // O of the last sub-chunk: its D^T was completed at the last step's barrier #2
+        if (nsub > 0) out_store<D, Act, Out>(L, a, nsub - 1, Ob, mcur, scale);
     }
+
     // The new conv window: rows n .. n+2 of (window ++ x), per channel.  This workgroup
     // rewrites the 16 v channels whose old window it read above, and one slice of the q | k
     // channels (whose old window only the prep kernel read, before this kernel started).  Each
@@ -941,11 +1073,11 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
     em.mark(2);
     if (d.conv_silu && conv_on)
         hipLaunchKernelGGL((chain_kernel<D, Act, Out, true>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
-                           dim3(256), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
+                           dim3(512), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
                            d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
     else
         hipLaunchKernelGGL((chain_kernel<D, Act, Out, false>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
-                           dim3(256), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
+                           dim3(512), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
                            d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
     em.mark(3);
     em.mark(4);  // the conv window is written by the chain kernel
