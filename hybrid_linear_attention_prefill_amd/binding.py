@@ -91,6 +91,7 @@ def _load():
                                              ctypes.POINTER(ctypes.c_void_p), I32]),
         "gdn_prefill_branches": (I32, [D, I32, ctypes.POINTER(ctypes.c_int64), V, V, V, V,
                                        ctypes.POINTER(S), ctypes.POINTER(S), V, V, SZ, V]),
+        "gdn_decode_step": (I32, [D, I32, V, V, V, V, ctypes.POINTER(S), ctypes.POINTER(S), V, V]),
         "gdn_commit_rows": (I64, [I64, I32]),
         "gdn_shared_prefix_rows": (I64, [I64, I64]),
         "gdn_ckpt_init": (I32, [R, I32]),
@@ -272,6 +273,17 @@ def gdn_prefill_branches(desc, cu_rows, x, conv_w, g, beta, inits, outs, o, ws, 
     st = lib.gdn_prefill_branches(ctypes.byref(desc), B, cu, _ptr(x), _ptr(conv_w), _ptr(g),
                                   _ptr(beta), ip, op, _ptr(o), _ptr(ws), nbytes, _stream(stream))
     _check(st, "gdn_prefill_branches")
+
+
+def gdn_decode_step(desc, x, conv_w, g, beta, inits, outs, o, stream=None):
+    """One token for each of len(inits) sequences: x [B][C], g/beta [B][Hv], o [B][Hv][d_v];
+    outs[b] receives sequence b's state (it may be inits[b] itself)."""
+    B = len(inits)
+    ip = (ctypes.POINTER(gdn_state) * B)(*[ctypes.pointer(s.c) for s in inits])
+    op = (ctypes.POINTER(gdn_state) * B)(*[ctypes.pointer(s.c) for s in outs])
+    st = lib.gdn_decode_step(ctypes.byref(desc), B, _ptr(x), _ptr(conv_w), _ptr(g), _ptr(beta),
+                             ip, op, _ptr(o), _stream(stream))
+    _check(st, "gdn_decode_step")
 
 
 def gdn_commit_rows(n, grid):

@@ -427,6 +427,70 @@ gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_
     return GDN_OK;
 }
 
+gdn_status gdn_decode_step(const gdn_desc *d, int32_t B, const void *x, const void *conv_w,
+                           const float *g, const float *beta, const gdn_state *const *in,
+                           gdn_state *const *out, void *o, void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (B <= 0 || !in || !out || !x || !g || !beta || !o || (d->conv_width > 0 && !conv_w))
+        return GDN_EINVAL;
+    if (!aligned(x, 16) || !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4) ||
+        (d->conv_width > 0 && !aligned(conv_w, 16)))
+        return GDN_EINVAL;
+    for (int32_t b = 0; b < B; ++b) {
+        if ((st = check_state(*d, in[b]))) return st;
+        if (!out[b] || !out[b]->S || !aligned(out[b]->S, 4)) return GDN_EINVAL;
+        if (d->conv_width > 0 && (!out[b]->conv || !aligned(out[b]->conv, 16))) return GDN_EINVAL;
+    }
+    // out[b] is in[b] itself or disjoint from it, and disjoint from every other sequence's
+    // states: each workgroup reads and rewrites only its own sequence's tiles.
+    for (int32_t b = 0; b < B; ++b) {
+        if (!states_same(in[b], out[b]) && states_overlap(*d, in[b], out[b])) return GDN_EALIAS;
+        for (int32_t j = 0; j < B; ++j) {
+            if (j == b) continue;
+            if (states_overlap(*d, out[b], in[j])) return GDN_EALIAS;
+            if (j < b && states_overlap(*d, out[b], out[j])) return GDN_EALIAS;
+        }
+    }
+    std::vector<int64_t> pos0((size_t)B);
+    for (int32_t b = 0; b < B; ++b) pos0[b] = in[b]->pos;
+    const uint64_t tag = gdn_desc_tag(d);
+    const int64_t C = n_channels(*d);
+    const size_t xb = (size_t)C * act_size(*d), ob = (size_t)d->n_v_heads * d->d_v * out_size(*d);
+    for (int32_t b0 = 0; b0 < B; b0 += kMaxSegPerLaunch) {
+        const int32_t n = std::min<int32_t>(kMaxSegPerLaunch, B - b0);
+        DecodeArgs da;
+        SegArgs wa;
+        std::memset(&da, 0, sizeof(da));
+        std::memset(&wa, 0, sizeof(wa));
+        for (int32_t i = 0; i < n; ++i) {
+            const int32_t b = b0 + i;
+            DecodeSeq &q = da.seq[i];
+            q.x = (const char *)x + (size_t)b * xb;
+            q.S_in = in[b]->S;
+            q.S_out = out[b]->S;
+            q.win = in[b]->conv;
+            q.g = g + (size_t)b * d->n_v_heads;
+            q.beta = beta + (size_t)b * d->n_v_heads;
+            q.o = (char *)o + (size_t)b * ob;
+            Seg &w = wa.seg[i];
+            w.row0 = b;  // row b of x
+            w.n = 1;
+            w.win_in = in[b]->conv;
+            w.win_out = out[b]->conv;
+        }
+        da.n = n;
+        wa.n_seg = d->conv_width > 0 ? n : 0;
+        if (launch_decode(*d, da, wa, x, conv_w, stream) != 0) return GDN_EDEVICE;
+    }
+    for (int32_t b = 0; b < B; ++b) {
+        out[b]->pos = pos0[b] + 1;
+        out[b]->tag = tag;
+    }
+    return GDN_OK;
+}
+
 int64_t gdn_commit_rows(int64_t n, int32_t grid)
 {
     if (n < 0 || grid <= 0) return -1;

@@ -50,6 +50,22 @@ struct Workspace {
     float *Fac;    // [n_sub][Hv][4][64]  per row: beta, beta*gamma, gamma, exp(G_n - G) (fp32)
 };
 
+// One sequence of a decode launch: its input row, state, window and outputs (device).
+struct DecodeSeq {
+    const void *x;       // [C] the token's pre-conv row
+    const float *S_in;   // [Hv][d_k][d_v]
+    float *S_out;        // may equal S_in
+    const void *win;     // [W-1][C] the window before the step (null without conv)
+    const float *g;      // [Hv]
+    const float *beta;   // [Hv]
+    void *o;             // [Hv][d_v]
+};
+
+struct DecodeArgs {
+    int32_t n;
+    DecodeSeq seq[kMaxSegPerLaunch];
+};
+
 size_t workspace_bytes(const gdn_desc &d, int64_t n_sub);
 Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base);
 
@@ -58,6 +74,10 @@ Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base);
 int launch_prefill(const gdn_desc &d, const SegArgs &sa, const void *x, const void *conv_w,
                    const float *g, const float *beta, void *o, const Workspace &ws,
                    void *stream, void *const *events = nullptr, int n_events = 0);
+// One decode step of da.n sequences (state and outputs), then the window shift of each
+// sequence (window_out = rows 1 .. W-1 of window_in ++ x) when windows are given in `win`.
+int launch_decode(const gdn_desc &d, const DecodeArgs &da, const SegArgs &win, const void *x,
+                  const void *conv_w, void *stream);
 int launch_conv_step(const gdn_desc &d, const void *x, const void *conv_w, void *window, void *y,
                      int64_t T, void *stream);
 int launch_zero(void *p, size_t bytes, void *stream);

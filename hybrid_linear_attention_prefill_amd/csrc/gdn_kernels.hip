@@ -1027,6 +1027,137 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const Act *__restrict__ 
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// decode_kernel: one token of one sequence per grid row, one (value head, 32-column tile of S)
+// per workgroup.  The per-token rule in fp32:
+//   q, k, v = conv(window ++ x) of the token; q^ = q / sqrt(|q|^2 + eps), k^ likewise;
+//   u = S^T k^;  e = v - e^g u;  S' = e^g S + beta k^ e^T;  o = scale S'^T q^
+// (S' = e^g (I - beta k^ k^T) S + beta k^ v^T).  Thread (r, j) = (t / 32, t % 32) holds column
+// j of the tile at rows r, r + 8, r + 16, ...: every load and store of S is 8 rows x 128
+// contiguous bytes, and the two column sums (u and o) finish with an 8-way sum through LDS in
+// a fixed order.  The conv window is not written here (several workgroups read the q | k
+// window of a key head); window_kernel shifts it afterwards.
+// ------------------------------------------------------------------------------------------
+template <int D, typename Act, typename Out, bool SILU>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs da, const Act *__restrict__ conv_w,
+                                                     int conv_on, int Hk, int Hv, float scale,
+                                                     float eps)
+{
+    constexpr int W = 32, NT = D / W, RPT = D / 8;
+    __shared__ float qk[2 * D];  // q^ | k^ of the key head
+    __shared__ float ve[W];      // conv(v) of the tile, then e
+    __shared__ float red[8][W];  // column partial sums of the 8 row groups
+    __shared__ float ssq[8];     // squared norms, per wave
+    const int h = blockIdx.x / NT, tile = blockIdx.x % NT, b = blockIdx.y;
+    const DecodeSeq sq = da.seq[b];
+    const int kh = h / (Hv / Hk), C = 2 * Hk * D + Hv * D;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const Act *x = (const Act *)sq.x, *win = (const Act *)sq.win;
+    auto conv1 = [&](int ch) -> float {
+        const float xv = to_f32(x[ch]);
+        if (!conv_on) return xv;
+        float y = to_f32(conv_w[ch * 4 + 0]) * to_f32(win[ch]) + to_f32(conv_w[ch * 4 + 1]) * to_f32(win[C + ch]) +
+                  to_f32(conv_w[ch * 4 + 2]) * to_f32(win[2 * C + ch]) + to_f32(conv_w[ch * 4 + 3]) * xv;
+        if constexpr (SILU) y = y / (1.f + expf(-y));
+        return y;
+    };
+    // 1. conv of q | k (2D channels) and of the tile's 32 v channels
+    float y = 0.f;
+    if (t < 2 * D) y = conv1((t < D ? 0 : Hk * D) + kh * D + t % D);
+    if (t < W) ve[t] = conv1(2 * Hk * D + h * D + tile * W + t);
+    float s2 = y * y;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
+    if (lane == 0) ssq[wave] = s2;
+    __syncthreads();
+    // 2. L2 norms: waves 0 .. D/64-1 hold q, the next D/64 waves hold k
+    if (t < 2 * D) {
+        float ss = 0.f;
+        const int w0 = (t < D) ? 0 : D / 64;
+#pragma unroll
+        for (int w = 0; w < D / 64; ++w) ss += ssq[w0 + w];
+        qk[t] = y / sqrtf(ss + eps);
+    }
+    const float alpha = expf(sq.g[h]), bt = sq.beta[h];
+    // 3. this thread's column of S; u = S^T k^
+    const int r = t / W, j = t % W;
+    const float *Sin = sq.S_in + (int64_t)h * D * D + tile * W + j;
+    float sv[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) sv[i] = Sin[(int64_t)(r + 8 * i) * D];
+    __syncthreads();  // q^ and k^ in LDS
+    float pu = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) pu += qk[D + r + 8 * i] * sv[i];
+    red[r][j] = pu;
+    __syncthreads();
+    if (t < W) {
+        float u = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u += red[q][t];
+        ve[t] = ve[t] - alpha * u;  // e
+    }
+    __syncthreads();
+    // 4. S' = e^g S + beta k^ e^T, stored; o = scale S'^T q^
+    const float ej = ve[j];
+    float *Sout = sq.S_out + (int64_t)h * D * D + tile * W + j;
+    float po = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int d = r + 8 * i;
+        const float sn = alpha * sv[i] + bt * qk[D + d] * ej;
+        Sout[(int64_t)d * D] = sn;
+        po += qk[d] * sn;
+    }
+    red[r][j] = po;
+    __syncthreads();
+    if (t < W) {
+        float ov = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ov += red[q][t];
+        store_out((Out *)sq.o + h * D + tile * W + t, ov * scale);
+    }
+}
+
+template <int D, typename Act, typename Out>
+static int decode_t(const gdn_desc &d, const DecodeArgs &da, const SegArgs &wa, const void *x,
+                    const void *conv_w, hipStream_t st)
+{
+    const int conv_on = d.conv_width > 0 ? 1 : 0;
+    const dim3 grid((D / 32) * d.n_v_heads, da.n);
+    if (d.conv_silu && conv_on)
+        hipLaunchKernelGGL((decode_kernel<D, Act, Out, true>), grid, dim3(256), 0, st, da,
+                           (const Act *)conv_w, conv_on, d.n_k_heads, d.n_v_heads, d.scale, d.l2_eps);
+    else
+        hipLaunchKernelGGL((decode_kernel<D, Act, Out, false>), grid, dim3(256), 0, st, da,
+                           (const Act *)conv_w, conv_on, d.n_k_heads, d.n_v_heads, d.scale, d.l2_eps);
+    if (conv_on && wa.n_seg > 0) {
+        const int C = 2 * d.n_k_heads * d.d_k + d.n_v_heads * d.d_v;
+        hipLaunchKernelGGL((window_kernel<Act>), dim3((C + 255) / 256, wa.n_seg), dim3(256), 0, st,
+                           wa, (const Act *)x, C);
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_decode(const gdn_desc &d, const DecodeArgs &da, const SegArgs &wa, const void *x,
+                  const void *conv_w, void *stream)
+{
+    (void)hipGetLastError();
+    hipStream_t st = (hipStream_t)stream;
+    if (d.d_k == 128) {
+        if (d.act_dtype == GDN_BF16)
+            return d.out_dtype == GDN_BF16 ? decode_t<128, bf16_t, bf16_t>(d, da, wa, x, conv_w, st)
+                                           : decode_t<128, bf16_t, float>(d, da, wa, x, conv_w, st);
+        return d.out_dtype == GDN_BF16 ? decode_t<128, float, bf16_t>(d, da, wa, x, conv_w, st)
+                                       : decode_t<128, float, float>(d, da, wa, x, conv_w, st);
+    }
+    if (d.act_dtype == GDN_BF16)
+        return d.out_dtype == GDN_BF16 ? decode_t<64, bf16_t, bf16_t>(d, da, wa, x, conv_w, st)
+                                       : decode_t<64, bf16_t, float>(d, da, wa, x, conv_w, st);
+    return d.out_dtype == GDN_BF16 ? decode_t<64, float, bf16_t>(d, da, wa, x, conv_w, st)
+                                   : decode_t<64, float, float>(d, da, wa, x, conv_w, st);
+}
+
 __global__ void zero_kernel(uint32_t *p, size_t n_words)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;

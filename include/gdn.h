@@ -189,6 +189,29 @@ gdn_status gdn_prefill_branches(const gdn_desc *desc, int32_t B, const int64_t *
                                 gdn_state *const *out, void *o, void *ws, size_t ws_bytes,
                                 void *stream);
 
+/* ---------------------------------------------------------------- decode */
+
+/* One-token step of B sequences, each from its own state: the width-W conv with the window
+ * carried, the L2 norm of q and k, then for every value head one step of the gated delta
+ * rule in fp32,
+ *   S <- e^g (I - beta k k^T) S + beta k v^T,   o = scale S^T q,
+ * the per-token rule the chunked prefill reaches by its chunk algebra.  It is the step that
+ * follows a fork's prefill when the small model answers on top of a session ("The shadow
+ * reader", section "Who asks": the fork decodes token by token, eagerly).
+ *
+ * x [B][C] (one row per sequence), g/beta [B][Hv], o [B][Hv][d_v] device.  in[b] is read,
+ * out[b] receives the advanced state (pos = in[b]->pos + 1, the tag kept); out[b] may be
+ * in[b] itself (in place).  in entries may repeat (a shared read-only state), but no out[b]
+ * may overlap an in[j] or out[j] of another sequence (GDN_EALIAS).  There is no position
+ * constraint: a decoded state sits off the 64-row grid, so only further decode steps
+ * continue it (a prefill refuses it with GDN_EGRID).  The result matches the per-token rule
+ * to fp32 rounding; it is not bitwise a GDN_FORK prefill of the same row, whose chunk
+ * algebra rounds differently.  Two kernels per group of at most 32 sequences: the step,
+ * then the window shift. */
+gdn_status gdn_decode_step(const gdn_desc *desc, int32_t B, const void *x, const void *conv_w,
+                           const float *g, const float *beta, const gdn_state *const *in,
+                           gdn_state *const *out, void *o, void *stream);
+
 /* ---------------------------------------------------------------- host scheduling (no device) */
 
 /* Rows a COMMIT from an aligned position absorbs out of n available rows:

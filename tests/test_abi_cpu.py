@@ -148,6 +148,38 @@ def test_branches_validation():
     assert call(1, [0, 10], [ctypes.pointer(foreign)]) == b.GDN_EMISMATCH
 
 
+def test_decode_validation_refuses_before_device_work():
+    d = layer_desc()
+    a = _state(pos=700)
+    c = _state(pos=33, S=FAKE + (20 << 30), conv=FAKE + (21 << 30))
+    ap, cp = ctypes.pointer(a), ctypes.pointer(c)
+
+    def call(B, inits, outs, x=FAKE, conv_w=FAKE, g=FAKE, beta=FAKE, o=FAKE, desc=d):
+        ia = None if inits is None else (ctypes.POINTER(b.gdn_state) * max(B, 1))(*inits)
+        oa = None if outs is None else (ctypes.POINTER(b.gdn_state) * max(B, 1))(*outs)
+        return b.lib.gdn_decode_step(ctypes.byref(desc), B, x, conv_w, g, beta, ia, oa, o, None)
+
+    assert call(0, [ap], [ap]) == b.GDN_EINVAL
+    assert call(1, None, [ap]) == b.GDN_EINVAL
+    assert call(1, [ap], None) == b.GDN_EINVAL
+    for kw in (dict(x=None), dict(g=None), dict(beta=None), dict(o=None), dict(conv_w=None),
+               dict(x=FAKE + 2), dict(o=FAKE + 8), dict(g=FAKE + 2), dict(conv_w=FAKE + 4)):
+        assert call(1, [ap], [ap], **kw) == b.GDN_EINVAL, kw
+    foreign = _state(tag=77)
+    assert call(1, [ctypes.pointer(foreign)], [ctypes.pointer(foreign)]) == b.GDN_EMISMATCH
+    # a shared input updated in place by one sequence while another reads it
+    assert call(2, [ap, ap], [ap, cp]) == b.GDN_EALIAS
+    # two sequences writing the same state
+    assert call(2, [ap, cp], [ctypes.pointer(_state(S=FAKE + (22 << 30), conv=FAKE + (23 << 30)))] * 2) == b.GDN_EALIAS
+    # an output overlapping its own input without being it
+    part = _state(pos=700, S=FAKE + 256, conv=FAKE + (24 << 30))
+    assert call(1, [ap], [ctypes.pointer(part)]) == b.GDN_EALIAS
+    # output state with a misaligned window
+    bad = _state(S=FAKE + (25 << 30), conv=FAKE + (26 << 30) + 8)
+    assert call(1, [ap], [ctypes.pointer(bad)]) == b.GDN_EINVAL
+    assert (a.pos, c.pos, part.pos) == (700, 33, 700)
+
+
 def test_state_ops_validation():
     d = layer_desc()
     live = _state(pos=512)
