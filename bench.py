@@ -15,7 +15,8 @@ average duration, from HIP events the library records on the launch stream aroun
 kernel in every timed step), the same figure for the whole layer call, and the float64 CPU
 oracle timed on a bounded sample of the same workload.
 
-    --extras                also time state capture/restore and a 370-row fork
+    --extras                also time state capture/restore, a 370-row fork and decode steps
+                            of 1 and 32 sessions
     --copy-calibration N    run a plain N-byte device copy after timing (for counter scaling)
 """
 import argparse
@@ -114,7 +115,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", action="store_true",
-                    help="also time state capture/restore and a 370-row fork")
+                    help="also time state capture/restore, a 370-row fork and decode "
+                         "steps of 1 and 32 sessions")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run a plain device copy of BYTES bytes three "
                          "times (reference dispatch for the HBM byte counters)")
@@ -208,6 +210,38 @@ def main():
         torch.cuda.synchronize()
         extras = {"state_capture_restore_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
                   "fork_370_rows_ms": round(e2.elapsed_time(e3) / reps2, 4)}
+        # decode steps of B sessions, each from its own forked state, in place: the step
+        # streams every session's fp32 state in and out, so it is HBM-bound for large B
+        C = desc.channels
+        # (two states per session, stepped back and forth: one launch per step)
+        for B in (1, 32):
+            ping = [b.State(desc) for _ in range(B)]
+            pong = [b.State(desc) for _ in range(B)]
+            for st_ in ping:
+                b.gdn_state_capture(desc, state, st_)
+            s = sets[0]
+            xb, gb, bb = s["x"][:B].contiguous(), s["g"][:B].contiguous(), s["beta"][:B].contiguous()
+            ob = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
+            for i in range(4):
+                src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
+                b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
+            reps3 = 50
+            e2.record(stream)
+            for i in range(reps3):
+                src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
+                b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
+            e3.record(stream)
+            torch.cuda.synchronize()
+            step_ms = e2.elapsed_time(e3) / reps3
+            step_bytes = B * (2 * Hv * d * d * 4 + 2 * 3 * C * 2 + C * 2 + 2 * Hv * 4 + Hv * d * 2)
+            gbps = step_bytes / (step_ms * 1e-3) / 1e9
+            extras["decode_B%d" % B] = {
+                "us_per_step": round(step_ms * 1e3, 2),
+                "tokens_per_s": round(B / (step_ms * 1e-3), 1),
+                "algorithmic_bytes_per_step": step_bytes,
+                "achieved_GBps": round(gbps, 1),
+                "hbm_frac": round(gbps / HBM_PEAK_GBS, 4)}
+            del ping, pong
 
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters

@@ -440,7 +440,9 @@ gdn_status gdn_decode_step(const gdn_desc *d, int32_t B, const void *x, const vo
         return GDN_EINVAL;
     for (int32_t b = 0; b < B; ++b) {
         if ((st = check_state(*d, in[b]))) return st;
-        if (!out[b] || !out[b]->S || !aligned(out[b]->S, 4)) return GDN_EINVAL;
+        // the step moves S in 16-byte pieces
+        if (!aligned(in[b]->S, 16)) return GDN_EINVAL;
+        if (!out[b] || !out[b]->S || !aligned(out[b]->S, 16)) return GDN_EINVAL;
         if (d->conv_width > 0 && (!out[b]->conv || !aligned(out[b]->conv, 16))) return GDN_EINVAL;
     }
     // out[b] is in[b] itself or disjoint from it, and disjoint from every other sequence's
@@ -471,17 +473,23 @@ gdn_status gdn_decode_step(const gdn_desc *d, int32_t B, const void *x, const vo
             q.S_in = in[b]->S;
             q.S_out = out[b]->S;
             q.win = in[b]->conv;
+            // a window other than the one read is written by the step itself
+            const bool sep = d->conv_width > 0 &&
+                             !overlap(in[b]->conv, gdn_state_conv_bytes(d), out[b]->conv,
+                                      gdn_state_conv_bytes(d));
+            q.win_out = sep ? out[b]->conv : nullptr;
             q.g = g + (size_t)b * d->n_v_heads;
             q.beta = beta + (size_t)b * d->n_v_heads;
             q.o = (char *)o + (size_t)b * ob;
-            Seg &w = wa.seg[i];
-            w.row0 = b;  // row b of x
-            w.n = 1;
-            w.win_in = in[b]->conv;
-            w.win_out = out[b]->conv;
+            if (d->conv_width > 0 && !sep) {  // in-place window: shifted by a second kernel
+                Seg &w = wa.seg[wa.n_seg++];
+                w.row0 = b;  // row b of x
+                w.n = 1;
+                w.win_in = in[b]->conv;
+                w.win_out = out[b]->conv;
+            }
         }
         da.n = n;
-        wa.n_seg = d->conv_width > 0 ? n : 0;
         if (launch_decode(*d, da, wa, x, conv_w, stream) != 0) return GDN_EDEVICE;
     }
     for (int32_t b = 0; b < B; ++b) {

@@ -56,6 +56,8 @@ struct DecodeSeq {
     const float *S_in;   // [Hv][d_k][d_v]
     float *S_out;        // may equal S_in
     const void *win;     // [W-1][C] the window before the step (null without conv)
+    void *win_out;       // [W-1][C] the window after the step, written by the step itself;
+                         // null when the shift runs as a separate kernel (in-place windows)
     const float *g;      // [Hv]
     const float *beta;   // [Hv]
     void *o;             // [Hv][d_v]

@@ -1032,89 +1032,128 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const Act *__restrict__ 
 // per workgroup.  The per-token rule in fp32:
 //   q, k, v = conv(window ++ x) of the token; q^ = q / sqrt(|q|^2 + eps), k^ likewise;
 //   u = S^T k^;  e = v - e^g u;  S' = e^g S + beta k^ e^T;  o = scale S'^T q^
-// (S' = e^g (I - beta k^ k^T) S + beta k^ v^T).  Thread (r, j) = (t / 32, t % 32) holds column
-// j of the tile at rows r, r + 8, r + 16, ...: every load and store of S is 8 rows x 128
-// contiguous bytes, and the two column sums (u and o) finish with an 8-way sum through LDS in
-// a fixed order.  The conv window is not written here (several workgroups read the q | k
-// window of a key head); window_kernel shifts it afterwards.
+// (S' = e^g (I - beta k^ k^T) S + beta k^ v^T).  Thread (r, c) = (t / 8, t % 8) holds columns
+// 4c .. 4c+3 of the tile at rows r, r + 32, ...: each of its loads and stores of S is 16 bytes,
+// and a wave's covers 8 rows x 128 contiguous bytes.  The column sums u and o are reduced
+// over the 8 row groups of a wave by lane swaps, then over the 4 waves through LDS, in a fixed
+// order.  The new conv window (the last W-1 inputs) is written here only into a window other
+// than the one read (several workgroups read the q | k window of a key head): the workgroup of
+// tile 0 of a key head's first value head writes the q | k channels, every workgroup its own v
+// channels.  For an in-place window, window_kernel shifts it afterwards.
 // ------------------------------------------------------------------------------------------
 template <int D, typename Act, typename Out, bool SILU>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs da, const Act *__restrict__ conv_w,
                                                      int conv_on, int Hk, int Hv, float scale,
                                                      float eps)
 {
-    constexpr int W = 32, NT = D / W, RPT = D / 8;
-    __shared__ float qk[2 * D];  // q^ | k^ of the key head
-    __shared__ float ve[W];      // conv(v) of the tile, then e
-    __shared__ float red[8][W];  // column partial sums of the 8 row groups
-    __shared__ float ssq[8];     // squared norms, per wave
+    constexpr int W = 32, NT = D / W, RPT = D / 32;
+    constexpr int NQK = 2 * D / 8;  // threads converting 8 q | k channels each
+    __shared__ float qk[2 * D];      // q | k of the key head after the conv (not yet normalised)
+    __shared__ float ve[W];          // conv(v) of the tile, then e
+    __shared__ float red[4][W];      // column partial sums of the 4 waves
+    __shared__ float inv[2];         // 1 / sqrt(|q|^2 + eps), 1 / sqrt(|k|^2 + eps)
     const int h = blockIdx.x / NT, tile = blockIdx.x % NT, b = blockIdx.y;
     const DecodeSeq sq = da.seq[b];
     const int kh = h / (Hv / Hk), C = 2 * Hk * D + Hv * D;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const Act *x = (const Act *)sq.x, *win = (const Act *)sq.win;
-    auto conv1 = [&](int ch) -> float {
-        const float xv = to_f32(x[ch]);
-        if (!conv_on) return xv;
-        float y = to_f32(conv_w[ch * 4 + 0]) * to_f32(win[ch]) + to_f32(conv_w[ch * 4 + 1]) * to_f32(win[C + ch]) +
-                  to_f32(conv_w[ch * 4 + 2]) * to_f32(win[2 * C + ch]) + to_f32(conv_w[ch * 4 + 3]) * xv;
-        if constexpr (SILU) y = y / (1.f + expf(-y));
-        return y;
-    };
-    // 1. conv of q | k (2D channels) and of the tile's 32 v channels
-    float y = 0.f;
-    if (t < 2 * D) y = conv1((t < D ? 0 : Hk * D) + kh * D + t % D);
-    if (t < W) ve[t] = conv1(2 * Hk * D + h * D + tile * W + t);
-    float s2 = y * y;
+    // this thread's part of the S tile, loaded first so that it is in flight during the conv
+    const int r = t / 8, c4 = 4 * (t % 8);
+    const f32x4 *Sin = (const f32x4 *)(sq.S_in + (int64_t)h * D * D + tile * W + c4);
+    f32x4 sv[RPT];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
-    if (lane == 0) ssq[wave] = s2;
+    for (int i = 0; i < RPT; ++i) sv[i] = Sin[(int64_t)(r + 32 * i) * (D / 4)];
+    // 1. conv: threads 0 .. NQK-1 take 8 q | k channels each, the next 4 threads 8 channels of
+    //    the tile's v; 16-byte loads of the row, the window rows and the taps
+    const int vt = t - NQK;
+    if (t < NQK || (vt >= 0 && vt < 4)) {
+        const int ch = t < NQK ? (8 * t < D ? 0 : Hk * D) + kh * D + (8 * t) % D
+                               : 2 * Hk * D + h * D + tile * W + 8 * vt;
+        float xr[8], w0r[8], w1r[8], w2r[8];
+        load8<Act>((const u32x4 *)x, ch, xr);
+        float y[8];
+        if (conv_on) {
+            load8<Act>((const u32x4 *)win, ch, w0r);
+            load8<Act>((const u32x4 *)(win + C), ch, w1r);
+            load8<Act>((const u32x4 *)(win + 2 * C), ch, w2r);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {  // taps of channels ch + 2q, ch + 2q + 1
+                float tp[8];
+                load8<Act>((const u32x4 *)conv_w, 4 * ch + 8 * q, tp);
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                    const int e = 2 * q + e2;
+                    float a = tp[4 * e2] * w0r[e] + tp[4 * e2 + 1] * w1r[e] + tp[4 * e2 + 2] * w2r[e] +
+                              tp[4 * e2 + 3] * xr[e];
+                    if constexpr (SILU) a = a / (1.f + expf(-a));
+                    y[e] = a;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = xr[e];
+        }
+        float *dst = t < NQK ? qk + 8 * t : ve + 8 * vt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dst[e] = y[e];
+        // the new window, when it is not the one read: the workgroup of tile 0 of a key
+        // head's first value head writes the q | k channels, every workgroup its own v ones
+        if (conv_on && sq.win_out != nullptr && (t >= NQK || (tile == 0 && h % (Hv / Hk) == 0))) {
+            Act *wo = (Act *)sq.win_out;
+            *(u32x4 *)(wo + ch) = *(const u32x4 *)(win + C + ch);
+            *(u32x4 *)(wo + C + ch) = *(const u32x4 *)(win + 2 * C + ch);
+            *(u32x4 *)(wo + 2 * C + ch) = *(const u32x4 *)(x + ch);
+            if constexpr (sizeof(Act) == 4) {
+                *(u32x4 *)(wo + ch + 4) = *(const u32x4 *)(win + C + ch + 4);
+                *(u32x4 *)(wo + C + ch + 4) = *(const u32x4 *)(win + 2 * C + ch + 4);
+                *(u32x4 *)(wo + 2 * C + ch + 4) = *(const u32x4 *)(x + ch + 4);
+            }
+        }
+    }
     __syncthreads();
-    // 2. L2 norms: waves 0 .. D/64-1 hold q, the next D/64 waves hold k
-    if (t < 2 * D) {
-        float ss = 0.f;
-        const int w0 = (t < D) ? 0 : D / 64;
+    // 2. L2 norms: wave 0 sums q^2, wave 1 k^2
+    if (wave < 2) {
+        float s2 = 0.f;
+        for (int i = lane; i < D; i += 64) s2 += qk[wave * D + i] * qk[wave * D + i];
 #pragma unroll
-        for (int w = 0; w < D / 64; ++w) ss += ssq[w0 + w];
-        qk[t] = y / sqrtf(ss + eps);
+        for (int off = 32; off > 0; off >>= 1) s2 += __shfl_xor(s2, off);
+        if (lane == 0) inv[wave] = 1.f / sqrtf(s2 + eps);
     }
     const float alpha = expf(sq.g[h]), bt = sq.beta[h];
-    // 3. this thread's column of S; u = S^T k^
-    const int r = t / W, j = t % W;
-    const float *Sin = sq.S_in + (int64_t)h * D * D + tile * W + j;
-    float sv[RPT];
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) sv[i] = Sin[(int64_t)(r + 8 * i) * D];
-    __syncthreads();  // q^ and k^ in LDS
-    float pu = 0.f;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) pu += qk[D + r + 8 * i] * sv[i];
-    red[r][j] = pu;
     __syncthreads();
-    if (t < W) {
-        float u = 0.f;
+    const float iq = inv[0], ik = inv[1];
+    // column sums of this thread's 4 columns over the wave's 8 row groups (lanes 8 apart),
+    // then over the 4 waves
+    auto colsum = [&](f32x4 p) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) u += red[q][t];
-        ve[t] = ve[t] - alpha * u;  // e
-    }
+        for (int off = 8; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p[e] += __shfl_xor(p[e], off);
+        if (lane < 8) *(f32x4 *)&red[wave][c4] = p;
+    };
+    // 3. u = S^T k^, then e = v - e^g u
+    f32x4 pu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) pu += (qk[D + r + 32 * i] * ik) * sv[i];
+    colsum(pu);
+    __syncthreads();
+    if (t < W) ve[t] = ve[t] - alpha * (((red[0][t] + red[1][t]) + red[2][t]) + red[3][t]);
     __syncthreads();
     // 4. S' = e^g S + beta k^ e^T, stored; o = scale S'^T q^
-    const float ej = ve[j];
-    float *Sout = sq.S_out + (int64_t)h * D * D + tile * W + j;
-    float po = 0.f;
+    const f32x4 ej = *(const f32x4 *)&ve[c4];
+    f32x4 *Sout = (f32x4 *)(sq.S_out + (int64_t)h * D * D + tile * W + c4);
+    f32x4 po = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int d = r + 8 * i;
-        const float sn = alpha * sv[i] + bt * qk[D + d] * ej;
-        Sout[(int64_t)d * D] = sn;
-        po += qk[d] * sn;
+        const int d = r + 32 * i;
+        const f32x4 sn = alpha * sv[i] + (bt * (qk[D + d] * ik)) * ej;
+        Sout[(int64_t)d * (D / 4)] = sn;
+        po += (qk[d] * iq) * sn;
     }
-    red[r][j] = po;
+    colsum(po);  // red was last read before the barrier above
     __syncthreads();
     if (t < W) {
-        float ov = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) ov += red[q][t];
+        const float ov = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
         store_out((Out *)sq.o + h * D + tile * W + t, ov * scale);
     }
 }

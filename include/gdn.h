@@ -199,15 +199,17 @@ gdn_status gdn_prefill_branches(const gdn_desc *desc, int32_t B, const int64_t *
  * follows a fork's prefill when the small model answers on top of a session ("The shadow
  * reader", section "Who asks": the fork decodes token by token, eagerly).
  *
- * x [B][C] (one row per sequence), g/beta [B][Hv], o [B][Hv][d_v] device.  in[b] is read,
+ * x [B][C] (one row per sequence), g/beta [B][Hv], o [B][Hv][d_v] device; S must be
+ * 16-byte aligned here (the step moves it in 16-byte pieces).  in[b] is read,
  * out[b] receives the advanced state (pos = in[b]->pos + 1, the tag kept); out[b] may be
  * in[b] itself (in place).  in entries may repeat (a shared read-only state), but no out[b]
  * may overlap an in[j] or out[j] of another sequence (GDN_EALIAS).  There is no position
  * constraint: a decoded state sits off the 64-row grid, so only further decode steps
  * continue it (a prefill refuses it with GDN_EGRID).  The result matches the per-token rule
  * to fp32 rounding; it is not bitwise a GDN_FORK prefill of the same row, whose chunk
- * algebra rounds differently.  Two kernels per group of at most 32 sequences: the step,
- * then the window shift. */
+ * algebra rounds differently.  One kernel per group of at most 32 sequences, plus a
+ * window-shift kernel when some out[b] shares its window with in[b] (in place): ping-pong
+ * between two states per session to keep one launch per step. */
 gdn_status gdn_decode_step(const gdn_desc *desc, int32_t B, const void *x, const void *conv_w,
                            const float *g, const float *beta, const gdn_state *const *in,
                            gdn_state *const *out, void *o, void *stream);

@@ -177,6 +177,9 @@ def test_decode_validation_refuses_before_device_work():
     # output state with a misaligned window
     bad = _state(S=FAKE + (25 << 30), conv=FAKE + (26 << 30) + 8)
     assert call(1, [ap], [ctypes.pointer(bad)]) == b.GDN_EINVAL
+    # S only 4-byte aligned: enough for a prefill, not for the step's 16-byte accesses
+    s4 = _state(pos=5, S=FAKE + (27 << 30) + 4, conv=FAKE + (28 << 30))
+    assert call(1, [ctypes.pointer(s4)], [ctypes.pointer(s4)]) == b.GDN_EINVAL
     assert (a.pos, c.pos, part.pos) == (700, 33, 700)
 
 
