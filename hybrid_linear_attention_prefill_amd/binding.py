@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn_prefill.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
 GDN_OK, GDN_EINVAL, GDN_ESHAPE, GDN_EGRID = 0, -1, -2, -3
-GDN_EMISMATCH, GDN_EWORKSPACE, GDN_EDEVICE, GDN_EALIAS = -4, -5, -6, -7
+GDN_EMISMATCH, GDN_EWORKSPACE, GDN_EDEVICE, GDN_EALIAS, GDN_EFILE = -4, -5, -6, -7, -8
 GDN_F32, GDN_BF16 = 0, 1
 GDN_COMMIT, GDN_FORK = 0, 1
 SUB_CHUNK = 64
@@ -92,6 +92,12 @@ def _load():
         "gdn_prefill_branches": (I32, [D, I32, ctypes.POINTER(ctypes.c_int64), V, V, V, V,
                                        ctypes.POINTER(S), ctypes.POINTER(S), V, V, SZ, V]),
         "gdn_decode_step": (I32, [D, I32, V, V, V, V, ctypes.POINTER(S), ctypes.POINTER(S), V, V]),
+        "gdn_state_file_header_bytes": (SZ, []),
+        "gdn_state_file_write": (I32, [D, V, V, I64, ctypes.c_uint64, ctypes.c_char_p]),
+        "gdn_state_file_read": (I32, [D, V, V, ctypes.POINTER(ctypes.c_int64), ctypes.c_uint64,
+                                      ctypes.c_char_p]),
+        "gdn_state_save": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
+        "gdn_state_load": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
         "gdn_commit_rows": (I64, [I64, I32]),
         "gdn_shared_prefix_rows": (I64, [I64, I64]),
         "gdn_ckpt_init": (I32, [R, I32]),
@@ -284,6 +290,47 @@ def gdn_decode_step(desc, x, conv_w, g, beta, inits, outs, o, stream=None):
     st = lib.gdn_decode_step(ctypes.byref(desc), B, _ptr(x), _ptr(conv_w), _ptr(g), _ptr(beta),
                              ip, op, _ptr(o), _stream(stream))
     _check(st, "gdn_decode_step")
+
+
+def gdn_state_file_header_bytes():
+    return lib.gdn_state_file_header_bytes()
+
+
+def _np_ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def gdn_state_file_write(desc, S_host, conv_host, pos, weights_hash, path):
+    """Host-buffer form: S_host [Hv][d_k][d_v] float32 and conv_host [W-1][C] numpy arrays of
+    the activation dtype's bytes (float32, or uint16 holding bf16 bits)."""
+    _check(lib.gdn_state_file_write(ctypes.byref(desc), _np_ptr(S_host), _np_ptr(conv_host),
+                                    int(pos), int(weights_hash), os.fsencode(path)),
+           "gdn_state_file_write")
+
+
+def gdn_state_file_read(desc, weights_hash, path):
+    """Returns (S [Hv][d_k][d_v] float32, window as raw numpy (float32 or uint16) or None, pos)."""
+    import numpy as np
+    S = np.empty((desc.n_v_heads, desc.d_k, desc.d_v), dtype=np.float32)
+    conv = None
+    if desc.conv_width > 0:
+        conv = np.empty((desc.conv_width - 1, desc.channels),
+                        dtype=np.uint16 if desc.act_dtype == GDN_BF16 else np.float32)
+    pos = ctypes.c_int64(-1)
+    _check(lib.gdn_state_file_read(ctypes.byref(desc), _np_ptr(S), _np_ptr(conv),
+                                   ctypes.byref(pos), int(weights_hash), os.fsencode(path)),
+           "gdn_state_file_read")
+    return S, conv, pos.value
+
+
+def gdn_state_save(desc, state, weights_hash, path, stream=None):
+    _check(lib.gdn_state_save(ctypes.byref(desc), state.ref(), int(weights_hash),
+                              os.fsencode(path), _stream(stream)), "gdn_state_save")
+
+
+def gdn_state_load(desc, state, weights_hash, path, stream=None):
+    _check(lib.gdn_state_load(ctypes.byref(desc), state.ref(), int(weights_hash),
+                              os.fsencode(path), _stream(stream)), "gdn_state_load")
 
 
 def gdn_commit_rows(n, grid):

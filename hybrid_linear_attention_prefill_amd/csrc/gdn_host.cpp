@@ -5,9 +5,15 @@
 // prefix", sections "Test Plan" and "Test Result").
 #include <hip/hip_runtime.h>
 
+#include <unistd.h>
+
 #include <algorithm>
+#include <cerrno>
+#include <cstddef>
 #include <cstdint>
+#include <cstdio>
 #include <cstring>
+#include <string>
 #include <vector>
 
 #include "gdn_internal.h"
@@ -152,6 +158,117 @@ static int64_t max_launch_subs(const std::vector<Seg> &segs)
         best = std::max(best, sub);
     }
     return best;
+}
+
+// ---------------------------------------------------------------- state files
+
+struct StateFileHeader {
+    char magic[8];
+    uint32_t version, header_bytes;
+    int32_t n_k_heads, n_v_heads, d_k, d_v, conv_width, sub_chunk, grid, act_dtype;
+    uint64_t tag, weights_hash;
+    int64_t pos;
+    uint64_t S_bytes, conv_bytes, payload_hash, header_hash;
+};
+static_assert(sizeof(StateFileHeader) == 104, "state file header layout");
+static const char kStateMagic[8] = {'G', 'D', 'N', 'S', 'T', 'A', 'T', '1'};
+
+static uint64_t fnv1a(uint64_t h, const void *p, size_t n)
+{
+    const unsigned char *c = (const unsigned char *)p;
+    for (size_t i = 0; i < n; ++i) {
+        h ^= c[i];
+        h *= 1099511628211ull;
+    }
+    return h;
+}
+static const uint64_t kFnvBasis = 1469598103934665603ull;
+
+static StateFileHeader make_header(const gdn_desc &d, int64_t pos, uint64_t weights_hash,
+                                   size_t s_bytes, size_t c_bytes)
+{
+    StateFileHeader h;
+    std::memset(&h, 0, sizeof(h));
+    std::memcpy(h.magic, kStateMagic, 8);
+    h.version = 1;
+    h.header_bytes = (uint32_t)sizeof(StateFileHeader);
+    h.n_k_heads = d.n_k_heads;
+    h.n_v_heads = d.n_v_heads;
+    h.d_k = d.d_k;
+    h.d_v = d.d_v;
+    h.conv_width = d.conv_width;
+    h.sub_chunk = d.sub_chunk;
+    h.grid = d.grid;
+    h.act_dtype = d.act_dtype;
+    h.tag = gdn_desc_tag(&d);
+    h.weights_hash = weights_hash;
+    h.pos = pos;
+    h.S_bytes = s_bytes;
+    h.conv_bytes = c_bytes;
+    return h;
+}
+
+static gdn_status write_state_file(const gdn_desc &d, const void *S, const void *conv,
+                                   int64_t pos, uint64_t weights_hash, const char *path)
+{
+    const size_t sb = gdn_state_S_bytes(&d), cb = gdn_state_conv_bytes(&d);
+    StateFileHeader h = make_header(d, pos, weights_hash, sb, cb);
+    h.payload_hash = fnv1a(fnv1a(kFnvBasis, S, sb), conv, cb);
+    h.header_hash = fnv1a(kFnvBasis, &h, offsetof(StateFileHeader, header_hash));
+    // a failed write must leave no file at `path`: remove the old one first
+    if (std::remove(path) != 0 && errno != ENOENT) return GDN_EFILE;
+    const std::string tmp = std::string(path) + ".tmp." + std::to_string((long)getpid());
+    FILE *f = std::fopen(tmp.c_str(), "wb");
+    if (!f) return GDN_EFILE;
+    bool ok = std::fwrite(&h, sizeof(h), 1, f) == 1 && std::fwrite(S, 1, sb, f) == sb &&
+              (cb == 0 || std::fwrite(conv, 1, cb, f) == cb);
+    ok = std::fflush(f) == 0 && ok;
+    ok = fsync(fileno(f)) == 0 && ok;
+    ok = std::fclose(f) == 0 && ok;
+    if (!ok || std::rename(tmp.c_str(), path) != 0) {
+        std::remove(tmp.c_str());
+        return GDN_EFILE;
+    }
+    return GDN_OK;
+}
+
+// Reads and verifies the file into host buffers S and conv (sized for `d`); nothing is written
+// to S, conv or *pos unless every check passes.
+static gdn_status read_state_file(const gdn_desc &d, void *S, void *conv, int64_t *pos,
+                                  uint64_t weights_hash, const char *path)
+{
+    const size_t sb = gdn_state_S_bytes(&d), cb = gdn_state_conv_bytes(&d);
+    FILE *f = std::fopen(path, "rb");
+    if (!f) return GDN_EFILE;
+    StateFileHeader h;
+    std::vector<unsigned char> payload;
+    gdn_status st = GDN_OK;
+    if (std::fread(&h, sizeof(h), 1, f) != 1 || std::memcmp(h.magic, kStateMagic, 8) != 0 ||
+        h.version != 1 || h.header_bytes != sizeof(h) ||
+        h.header_hash != fnv1a(kFnvBasis, &h, offsetof(StateFileHeader, header_hash))) {
+        st = GDN_EFILE;
+    } else {
+        const StateFileHeader want = make_header(d, h.pos, weights_hash, sb, cb);
+        if (h.n_k_heads != want.n_k_heads || h.n_v_heads != want.n_v_heads || h.d_k != want.d_k ||
+            h.d_v != want.d_v || h.conv_width != want.conv_width || h.sub_chunk != want.sub_chunk ||
+            h.grid != want.grid || h.act_dtype != want.act_dtype || h.tag != want.tag ||
+            h.weights_hash != want.weights_hash || h.S_bytes != sb || h.conv_bytes != cb) {
+            st = GDN_EMISMATCH;
+        } else if (h.pos < 0) {
+            st = GDN_EFILE;
+        } else {
+            payload.resize(sb + cb);
+            if (std::fread(payload.data(), 1, sb + cb, f) != sb + cb || std::fgetc(f) != EOF ||
+                fnv1a(kFnvBasis, payload.data(), sb + cb) != h.payload_hash)
+                st = GDN_EFILE;
+        }
+    }
+    std::fclose(f);
+    if (st) return st;
+    std::memcpy(S, payload.data(), sb);
+    if (cb) std::memcpy(conv, payload.data() + sb, cb);
+    *pos = h.pos;
+    return GDN_OK;
 }
 
 }  // namespace gdn
@@ -499,6 +616,66 @@ gdn_status gdn_decode_step(const gdn_desc *d, int32_t B, const void *x, const vo
     return GDN_OK;
 }
 
+size_t gdn_state_file_header_bytes(void) { return sizeof(StateFileHeader); }
+
+gdn_status gdn_state_file_write(const gdn_desc *d, const void *S_host, const void *conv_host,
+                                int64_t pos, uint64_t weights_hash, const char *path)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (!S_host || (d->conv_width > 0 && !conv_host) || !path || !*path || pos < 0)
+        return GDN_EINVAL;
+    return write_state_file(*d, S_host, conv_host, pos, weights_hash, path);
+}
+
+gdn_status gdn_state_file_read(const gdn_desc *d, void *S_host, void *conv_host, int64_t *pos,
+                               uint64_t weights_hash, const char *path)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (!S_host || (d->conv_width > 0 && !conv_host) || !pos || !path || !*path) return GDN_EINVAL;
+    return read_state_file(*d, S_host, conv_host, pos, weights_hash, path);
+}
+
+gdn_status gdn_state_save(const gdn_desc *d, const gdn_state *state, uint64_t weights_hash,
+                          const char *path, void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if ((st = check_state(*d, state))) return st;
+    if (!path || !*path) return GDN_EINVAL;
+    const size_t sb = gdn_state_S_bytes(d), cb = gdn_state_conv_bytes(d);
+    std::vector<unsigned char> host(sb + cb);
+    hipStream_t hs = (hipStream_t)stream;
+    if (hipMemcpyAsync(host.data(), state->S, sb, hipMemcpyDeviceToHost, hs) != hipSuccess ||
+        (cb && hipMemcpyAsync(host.data() + sb, state->conv, cb, hipMemcpyDeviceToHost, hs) != hipSuccess) ||
+        hipStreamSynchronize(hs) != hipSuccess)
+        return GDN_EDEVICE;
+    return write_state_file(*d, host.data(), host.data() + sb, state->pos, weights_hash, path);
+}
+
+gdn_status gdn_state_load(const gdn_desc *d, gdn_state *state, uint64_t weights_hash,
+                          const char *path, void *stream)
+{
+    gdn_status st = gdn_desc_check(d);
+    if (st) return st;
+    if (!state || !state->S || !aligned(state->S, 4)) return GDN_EINVAL;
+    if (d->conv_width > 0 && (!state->conv || !aligned(state->conv, 16))) return GDN_EINVAL;
+    if (!path || !*path) return GDN_EINVAL;
+    const size_t sb = gdn_state_S_bytes(d), cb = gdn_state_conv_bytes(d);
+    std::vector<unsigned char> host(sb + cb);
+    int64_t pos = 0;
+    if ((st = read_state_file(*d, host.data(), host.data() + sb, &pos, weights_hash, path))) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    if (hipMemcpyAsync(state->S, host.data(), sb, hipMemcpyHostToDevice, hs) != hipSuccess ||
+        (cb && hipMemcpyAsync(state->conv, host.data() + sb, cb, hipMemcpyHostToDevice, hs) != hipSuccess) ||
+        hipStreamSynchronize(hs) != hipSuccess)
+        return GDN_EDEVICE;
+    state->pos = pos;
+    state->tag = gdn_desc_tag(d);
+    return GDN_OK;
+}
+
 int64_t gdn_commit_rows(int64_t n, int32_t grid)
 {
     if (n < 0 || grid <= 0) return -1;
@@ -574,6 +751,7 @@ const char *gdn_status_str(gdn_status s)
     case GDN_EWORKSPACE: return "workspace missing or too small";
     case GDN_EDEVICE: return "HIP launch or copy failed";
     case GDN_EALIAS: return "output state overlaps memory it must not";
+    case GDN_EFILE: return "state file missing, unreadable, truncated, corrupt or not writable";
     default: return "unknown status";
     }
 }

@@ -62,6 +62,8 @@ enum {
     GDN_EWORKSPACE = -5, /* workspace missing or smaller than gdn_workspace_bytes() */
     GDN_EDEVICE = -6,    /* a HIP launch or copy failed */
     GDN_EALIAS = -7,     /* an output state overlaps memory it must not */
+    GDN_EFILE = -8,      /* a state file is missing, unreadable, truncated or corrupt, or
+                            cannot be written */
 };
 
 enum { GDN_F32 = 0, GDN_BF16 = 1 };  /* element types of x / conv / window and of o */
@@ -135,6 +137,44 @@ gdn_status gdn_state_restore(const gdn_desc *desc, gdn_state *live, const gdn_st
 /* dst[i] <- src for i in [0, n): n device copies (slots for a batch of branches). */
 gdn_status gdn_state_fork(const gdn_desc *desc, const gdn_state *src, gdn_state *dst, int32_t n,
                           void *stream);
+
+/* ---------------------------------------------------------------- state files */
+
+/* A state file holds one state (S, the conv window, pos) with a header that records the
+ * layer descriptor's fields and tag (heads, dims, conv width, sub-chunk, grid, act dtype) and a
+ * caller-chosen 64-bit hash of the model weights.  A file for another layer shape, grid,
+ * dtype or weights is refused (GDN_EMISMATCH) and the state is left as it was; a missing,
+ * short or corrupt file (FNV-1a checksums over header and payload) gives GDN_EFILE ("The
+ * shadow reader", sections "Memory and the disk" and "Memory": a session goes to disk and
+ * comes back exact, and a file for another model or grid is not read; "Long context and
+ * sessions", section "On disk, across reloads": a copy for other layers reads as missing,
+ * and a failed write leaves the slot missing, never stale).
+ *
+ * Writing first removes any file at `path`, then writes `path`.tmp.<pid>, flushes it to disk
+ * and renames it to `path`: a failed or interrupted write leaves no file at `path`.
+ * Layout (little-endian): a 104-byte header {char[8] "GDNSTAT1", u32 version = 1,
+ * u32 header bytes = 104, i32 n_k_heads, n_v_heads, d_k, d_v, conv_width, sub_chunk, grid,
+ * act_dtype, u64 tag, u64 weights_hash, i64 pos, u64 S bytes, u64 window bytes,
+ * u64 FNV-1a of the payload, u64 FNV-1a of the preceding 96 header bytes}, then S, then the
+ * window. */
+size_t gdn_state_file_header_bytes(void);
+
+/* Host-buffer forms: S_host [Hv][d_k][d_v] fp32 and conv_host [W-1][C] act dtype are host
+ * memory (conv_host may be NULL when conv_width == 0). */
+gdn_status gdn_state_file_write(const gdn_desc *desc, const void *S_host, const void *conv_host,
+                                int64_t pos, uint64_t weights_hash, const char *path);
+/* Reads and verifies the whole file before writing S_host, conv_host and *pos. */
+gdn_status gdn_state_file_read(const gdn_desc *desc, void *S_host, void *conv_host, int64_t *pos,
+                               uint64_t weights_hash, const char *path);
+
+/* Device forms: copy the state through host memory.  Both synchronise `stream` (work queued
+ * on it that writes the state completes first; a load's copy completes before returning).
+ * gdn_state_save refuses a state of another tag (GDN_EMISMATCH); gdn_state_load sets pos and
+ * tag only after the copy succeeded. */
+gdn_status gdn_state_save(const gdn_desc *desc, const gdn_state *state, uint64_t weights_hash,
+                          const char *path, void *stream);
+gdn_status gdn_state_load(const gdn_desc *desc, gdn_state *state, uint64_t weights_hash,
+                          const char *path, void *stream);
 
 /* ---------------------------------------------------------------- compute */
 

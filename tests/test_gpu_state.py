@@ -268,3 +268,28 @@ def test_refusals_enqueue_nothing(b, desc):
     o2, s2 = run_fork(b, desc, dinp, new_state(b, desc), ws=ws)
     torch.cuda.synchronize()
     assert same_bits(o1, o2) and same_bits(s1.S, s2.S)
+
+
+def test_state_file_round_trip_continues_exactly(b, desc, tmp_path):
+    """A session saved to a file and loaded into another slot continues bit for bit ("The
+    shadow reader", section "Memory": it comes back exact); a file for other weights is
+    refused and the slot keeps what it held."""
+    weights = 0xABCDEF0123456789
+    dinp = to_dev(synth.layer_inputs(SHAPE, 1536, seed=50))
+    ws = b.workspace(desc, 1536)
+    live = new_state(b, desc)
+    _commit(b, desc, dinp, live, 0, 1024, ws)
+    path = str(tmp_path / "session.gdn")
+    b.gdn_state_save(desc, live, weights, path)
+    slot = new_state(b, desc)
+    b.gdn_state_load(desc, slot, weights, path)
+    assert same_bits(slot.S, live.S) and same_bits(slot.conv, live.conv)
+    assert slot.pos == live.pos == 1024 and slot.tag == live.tag
+    _, o1 = _commit(b, desc, dinp, live, 1024, 1536, ws)
+    _, o2 = _commit(b, desc, dinp, slot, 1024, 1536, ws)
+    assert same_bits(o1, o2) and same_bits(slot.S, live.S)
+    keep = slot.S.clone()
+    with pytest.raises(b.GdnError) as e:
+        b.gdn_state_load(desc, slot, weights + 1, path)
+    assert e.value.status == b.GDN_EMISMATCH
+    assert same_bits(slot.S, keep) and slot.pos == 1536
