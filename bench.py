@@ -15,8 +15,8 @@ average duration, from HIP events the library records on the launch stream aroun
 kernel in every timed step), the same figure for the whole layer call, and the float64 CPU
 oracle timed on a bounded sample of the same workload.
 
-    --extras                also time state capture/restore, a 370-row fork and decode steps
-                            of 1 and 32 sessions
+    --extras                also time state capture/restore, a 370-row fork, decode steps
+                            of 1 and 32 sessions and the two projections
     --copy-calibration N    run a plain N-byte device copy after timing (for counter scaling)
 """
 import argparse
@@ -115,8 +115,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", action="store_true",
-                    help="also time state capture/restore, a 370-row fork and decode "
-                         "steps of 1 and 32 sessions")
+                    help="also time state capture/restore, a 370-row fork, decode "
+                         "steps of 1 and 32 sessions and the two projections")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run a plain device copy of BYTES bytes three "
                          "times (reference dispatch for the HBM byte counters)")
@@ -242,6 +242,27 @@ def main():
                 "achieved_GBps": round(gbps, 1),
                 "hbm_frac": round(gbps / HBM_PEAK_GBS, 4)}
             del ping, pong
+
+        # the layer's projections at the prefill length (bf16 in and out, fp32 accumulation)
+        for name, (K, N) in (("in_projection", (2048, 8256)), ("out_projection", (4096, 2048))):
+            px = torch.randn((T_ROWS, K), device=dev).to(torch.bfloat16)
+            pw = (torch.randn((N, K), device=dev) / K ** 0.5).to(torch.bfloat16)
+            py = torch.empty((T_ROWS, N), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                b.gdn_linear(px, pw, py)
+            reps4 = 20
+            e2.record(stream)
+            for _ in range(reps4):
+                b.gdn_linear(px, pw, py)
+            e3.record(stream)
+            torch.cuda.synchronize()
+            lin_ms = e2.elapsed_time(e3) / reps4
+            tflops = 2.0 * T_ROWS * K * N / (lin_ms * 1e-3) / 1e12
+            extras["linear_" + name] = {"T": T_ROWS, "K": K, "N": N,
+                                        "us": round(lin_ms * 1e3, 2),
+                                        "tflops": round(tflops, 1),
+                                        "mfma_bf16_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+            del px, pw, py
 
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters

@@ -98,6 +98,7 @@ def _load():
                                       ctypes.c_char_p]),
         "gdn_state_save": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
         "gdn_state_load": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
+        "gdn_linear": (I32, [I64, I32, I32, V, V, V, I32, V]),
         "gdn_commit_rows": (I64, [I64, I32]),
         "gdn_shared_prefix_rows": (I64, [I64, I64]),
         "gdn_ckpt_init": (I32, [R, I32]),
@@ -331,6 +332,14 @@ def gdn_state_save(desc, state, weights_hash, path, stream=None):
 def gdn_state_load(desc, state, weights_hash, path, stream=None):
     _check(lib.gdn_state_load(ctypes.byref(desc), state.ref(), int(weights_hash),
                               os.fsencode(path), _stream(stream)), "gdn_state_load")
+
+
+def gdn_linear(x, w, y, stream=None):
+    """y[T][N] = x[T][K] w[N][K]^T (x, w bf16 device tensors; y bf16 or float32)."""
+    T, K = x.shape
+    N = w.shape[0]
+    _check(lib.gdn_linear(int(T), int(K), int(N), _ptr(x), _ptr(w), _ptr(y),
+                          _DTYPE_CODE[y.dtype], _stream(stream)), "gdn_linear")
 
 
 def gdn_commit_rows(n, grid):

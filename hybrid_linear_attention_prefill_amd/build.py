@@ -2,8 +2,9 @@
 
     python -m hybrid_linear_attention_prefill_amd.build
 
-Compiles csrc/gdn_host.cpp (validation, scheduling, launches) and csrc/gdn_kernels.hip (the
-kernels) into hybrid_linear_attention_prefill_amd/libgdn_prefill.so.  Always recompiles.
+Compiles csrc/gdn_host.cpp (validation, scheduling, launches), csrc/gdn_kernels.hip (the
+layer's kernels) and csrc/gdn_linear.hip (the projection GEMM) into libgdn_prefill.so beside
+this file.  Always recompiles.
 """
 import os
 import subprocess
@@ -12,7 +13,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn_prefill.so")
-SOURCES = [os.path.join(PKG, "csrc", "gdn_host.cpp"), os.path.join(PKG, "csrc", "gdn_kernels.hip")]
+SOURCES = [os.path.join(PKG, "csrc", "gdn_host.cpp"), os.path.join(PKG, "csrc", "gdn_kernels.hip"),
+           os.path.join(PKG, "csrc", "gdn_linear.hip")]
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is switched off for all device code.

@@ -676,6 +676,18 @@ gdn_status gdn_state_load(const gdn_desc *d, gdn_state *state, uint64_t weights_
     return GDN_OK;
 }
 
+gdn_status gdn_linear(int64_t T, int32_t K, int32_t N, const void *x, const void *w, void *y,
+                      int32_t out_dtype, void *stream)
+{
+    if (T < 0 || K <= 0 || N <= 0 || K % 64 != 0 || N % 16 != 0) return GDN_EINVAL;
+    if (out_dtype != GDN_BF16 && out_dtype != GDN_F32) return GDN_EINVAL;
+    if (T > (int64_t)INT32_MAX * 128) return GDN_EINVAL;
+    if (T == 0) return GDN_OK;
+    if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return GDN_EINVAL;
+    if (launch_linear(T, K, N, x, w, y, out_dtype, stream) != 0) return GDN_EDEVICE;
+    return GDN_OK;
+}
+
 int64_t gdn_commit_rows(int64_t n, int32_t grid)
 {
     if (n < 0 || grid <= 0) return -1;

@@ -82,6 +82,9 @@ int launch_decode(const gdn_desc &d, const DecodeArgs &da, const SegArgs &win, c
                   const void *conv_w, void *stream);
 int launch_conv_step(const gdn_desc &d, const void *x, const void *conv_w, void *window, void *y,
                      int64_t T, void *stream);
+// y[T][N] = x[T][K] w[N][K]^T, bf16 in, fp32 accumulation, y in out_dtype (gdn_linear.hip).
+int launch_linear(int64_t T, int K, int N, const void *x, const void *w, void *y, int out_dtype,
+                  void *stream);
 int launch_zero(void *p, size_t bytes, void *stream);
 int launch_copy(void *dst, const void *src, size_t bytes, void *stream);
 

@@ -8,7 +8,7 @@ Draws use numpy's PCG64 seeded with ``[seed, stream]``; the stream ids are fixed
 
   0 q channels | 1 k channels | 2 v channels / embedding table | 3 beta logits |
   4 g logits | 5 conv weights | 6 token ids | 7 turn cuts | 8 question ids |
-  9 branch lengths | 10 divergence point
+  9 branch lengths | 10 divergence point | 11 projection inputs | 12 projection weights
 
 Value recipes (the pages print no data; these are stated stand-ins):
   x ~ N(0,1) cast to the activation dtype with round-to-nearest-even;
@@ -22,6 +22,7 @@ import torch
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_BETA, STREAM_G, STREAM_W = 0, 1, 2, 3, 4, 5
 STREAM_IDS, STREAM_CUTS, STREAM_QUESTION, STREAM_BRANCH, STREAM_DIVERGE = 6, 7, 8, 9, 10
+STREAM_PROJ_X, STREAM_PROJ_W = 11, 12
 
 
 @dataclass(frozen=True)
@@ -141,3 +142,11 @@ def branch_lengths(seed, n, lo=1, hi=200):
 
 def divergence_point(seed, lo, hi):
     return int(rng(seed, STREAM_DIVERGE).integers(lo, hi))
+
+
+def linear_inputs(T, K, N, seed=0):
+    """Inputs of a projection y = x w^T: x [T, K] ~ N(0,1) and w [N, K] ~ N(0, 1/K) (the usual
+    1/sqrt(fan-in) init), both cast to bf16 with round-to-nearest-even."""
+    x = cast(rng(seed, STREAM_PROJ_X).standard_normal((T, K)), torch.bfloat16)
+    w = cast(rng(seed, STREAM_PROJ_W).standard_normal((N, K)) / np.sqrt(K), torch.bfloat16)
+    return x, w

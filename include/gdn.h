@@ -254,6 +254,19 @@ gdn_status gdn_decode_step(const gdn_desc *desc, int32_t B, const void *x, const
                            const float *g, const float *beta, const gdn_state *const *in,
                            gdn_state *const *out, void *o, void *stream);
 
+/* ---------------------------------------------------------------- projections */
+
+/* y[T][N] = x[T][K] w[N][K]^T: the projections around the layer (hidden -> q|k|v|gate logits,
+ * and the output side), bf16 x and w, fp32 accumulation, y in out_dtype (GDN_BF16 or
+ * GDN_F32).  One tiling and one summation order over K for every T, so each row of y depends
+ * only on its row of x and on w: a run over any subset or grouping of rows gives the same
+ * bits as a run over all of them (PR "qwen3_5: run prompts that share prefixes once per
+ * prefix", section Purpose, "GEMMs": one fixed algorithm per weight shape, so grouped runs
+ * equal a plain pass bit for bit).  Requires K % 64 == 0, N % 16 == 0, T >= 0 (T == 0 does
+ * nothing); x, w, y device pointers, 16-byte aligned.  Asynchronous on `stream`. */
+gdn_status gdn_linear(int64_t T, int32_t K, int32_t N, const void *x, const void *w, void *y,
+                      int32_t out_dtype, void *stream);
+
 /* ---------------------------------------------------------------- host scheduling (no device) */
 
 /* Rows a COMMIT from an aligned position absorbs out of n available rows:

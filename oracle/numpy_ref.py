@@ -91,3 +91,13 @@ def gdn_layer(x, conv_w, window, g, beta, S0, *, n_k_heads, n_v_heads, d_k, d_v,
         o[:, h], S[h] = gated_delta_rule(qn[:, kh], kn[:, kh], v[:, h], np.asarray(g)[:, h],
                                          np.asarray(beta)[:, h], S0[h], scale)
     return o, S, win
+
+
+def linear(x, w):
+    """The projections around the layer: y[t, n] = sum_k x[t, k] w[n, k] (w as stored by a
+    linear layer, one row per output), in float64.  The pages fix one summation order per
+    weight shape so that grouped runs equal a plain pass (PR "qwen3_5: run prompts that share
+    prefixes once per prefix", section Purpose, "GEMMs"); the exact sum has no order."""
+    x = np.asarray(x, np.float64)
+    w = np.asarray(w, np.float64)
+    return x @ w.T

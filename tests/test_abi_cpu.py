@@ -183,6 +183,16 @@ def test_decode_validation_refuses_before_device_work():
     assert (a.pos, c.pos, part.pos) == (700, 33, 700)
 
 
+def test_linear_validation():
+    def call(T=64, K=128, N=32, x=FAKE, w=FAKE, y=FAKE, od=b.GDN_BF16):
+        return b.lib.gdn_linear(T, K, N, x, w, y, od, None)
+
+    for kw in (dict(K=96), dict(K=0), dict(N=24), dict(N=0), dict(T=-1), dict(od=5),
+               dict(x=None), dict(w=None), dict(y=None), dict(x=FAKE + 8), dict(y=FAKE + 4)):
+        assert call(**kw) == b.GDN_EINVAL, kw
+    assert call(T=0, x=None, w=None, y=None) == b.GDN_OK  # nothing to do, nothing touched
+
+
 def test_state_ops_validation():
     d = layer_desc()
     live = _state(pos=512)

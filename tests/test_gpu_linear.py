@@ -1,0 +1,95 @@
+"""The projections around the layer on the GPU (gdn_linear), through the C ABI.
+
+The pages want grouped runs (a shared prefix once, then each branch) to equal a plain pass over
+the full prompt bit for bit, which asks the projections to give every row the same bits however
+many rows share the call (PR "qwen3_5: run prompts that share prefixes once per prefix", section
+Purpose, "GEMMs").  Tested here: parity with the float64 oracle (a plain matmul on the exact
+bf16 inputs) and bitwise equality of every row between calls on different row ranges.
+"""
+import numpy as np
+import pytest
+import torch
+
+from hybrid_linear_attention_prefill_amd import synth
+from tests.helpers import TOL, rel_l2, same_bits
+
+pytestmark = pytest.mark.gpu
+
+# fp32 accumulation of K exact bf16 products: relative error ~ sqrt(K) * 2^-24, far below this
+FP32_TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def b():
+    from hybrid_linear_attention_prefill_amd import binding
+    assert torch.cuda.is_available()
+    return binding
+
+
+def _oracle(x, w, rows=None):
+    from oracle import numpy_ref
+    xs = synth.f64(x if rows is None else x[rows])
+    return numpy_ref.linear(xs, synth.f64(w))
+
+
+def _run(b, x, w, dtype):
+    y = torch.empty((x.shape[0], w.shape[0]), dtype=dtype, device="cuda")
+    b.gdn_linear(x, w, y)
+    return y
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("T,K,N", [(300, 256, 272), (1, 64, 16), (129, 192, 144), (64, 512, 128)])
+def test_linear_matches_oracle(b, T, K, N, dtype):
+    """Ragged row tiles (300 = 2 x 128 + 44), a 16-column tail tile, one row, one K step."""
+    x, w = synth.linear_inputs(T, K, N, seed=T + K)
+    y = _run(b, x.cuda(), w.cuda(), dtype)
+    torch.cuda.synchronize()
+    err = rel_l2(y.float().cpu().numpy(), _oracle(x, w))
+    print("linear T=%d K=%d N=%d %s rel_l2=%.3e" % (T, K, N, dtype, err), flush=True)
+    assert err < (FP32_TOL if dtype == torch.float32 else TOL)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_rows_are_invariant_to_the_call(b, dtype):
+    """Rows a .. b-1 computed alone equal the same rows of one call over all rows, bit for bit,
+    wherever the range starts and ends relative to the 128-row tiles."""
+    T, K, N = 300, 256, 272
+    x, w = synth.linear_inputs(T, K, N, seed=5)
+    xd, wd = x.cuda(), w.cuda()
+    full = _run(b, xd, wd, dtype)
+    for a, e in ((0, 1), (37, 300), (128, 256), (255, 257), (1, 129), (299, 300), (0, 300)):
+        part = _run(b, xd[a:e], wd, dtype)
+        assert same_bits(part, full[a:e]), (a, e)
+
+
+def test_zero_rows_and_output_untouched_outside(b):
+    x, w = synth.linear_inputs(8, 64, 32, seed=6)
+    y = torch.full((8, 32), 7.0, dtype=torch.float32, device="cuda")
+    b.gdn_linear(x.cuda()[:0], w.cuda(), y[:0])
+    torch.cuda.synchronize()
+    assert (y == 7.0).all()
+    # a 16-column output whose neighbours in memory are sentinels: nothing past N is written
+    buf = torch.full((8 * 16 + 64,), 3.0, dtype=torch.float32, device="cuda")
+    b.gdn_linear(x.cuda(), w.cuda()[:16], buf[:128].view(8, 16))
+    torch.cuda.synchronize()
+    assert (buf[128:] == 3.0).all()
+    assert rel_l2(buf[:128].view(8, 16).cpu().numpy(), _oracle(x, w[:16])) < FP32_TOL
+
+
+@pytest.mark.parametrize("name,T,K,N", [("in_projection", 8192, 2048, 8256),
+                                        ("out_projection", 8192, 4096, 2048)])
+def test_layer_projection_shapes_sampled(b, name, T, K, N):
+    """The layer's own projection shapes at the prefill length: 8,192 rows from a 2,048-wide
+    hidden state into q | k | v | beta | g (8,256 columns), and 4,096 value channels back to
+    2,048.  The oracle checks sampled rows; the row-invariance check runs a tail call."""
+    x, w = synth.linear_inputs(T, K, N, seed=7)
+    xd, wd = x.cuda(), w.cuda()
+    y = _run(b, xd, wd, torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 4095, 5000, 8190, 8191])
+    err = rel_l2(y[rows].float().cpu().numpy(), _oracle(x, w, rows))
+    print("%s sampled rel_l2=%.3e" % (name, err), flush=True)
+    assert err < TOL
+    tail = _run(b, xd[8000:], wd, torch.bfloat16)
+    assert same_bits(tail, y[8000:])

@@ -376,3 +376,25 @@ def test_head_subset_matches_full_run():
     os_, Ss, _ = c_oracle.gdn_layer(x, None, None, g, beta, S0, heads=[3, 1], **kw)
     for h in (1, 3):
         assert np.array_equal(os_[:, h], o[:, h]) and np.array_equal(Ss[h], S[h])
+
+
+def test_linear_against_brute_force_and_closed_forms():
+    """The projection's oracle against a triple loop, identity and permutation weights, and
+    linearity: a transposed operand or a dropped term fails one of these."""
+    from oracle import numpy_ref
+    r = np.random.default_rng(7)
+    x = r.standard_normal((5, 8))
+    w = r.standard_normal((3, 8))
+    y = numpy_ref.linear(x, w)
+    for t in range(5):
+        for n in range(3):
+            s = 0.0
+            for k in range(8):
+                s += x[t, k] * w[n, k]
+            assert abs(y[t, n] - s) < 1e-12
+    assert np.array_equal(numpy_ref.linear(x, np.eye(8)), x)
+    perm = np.eye(8)[[3, 1, 7]]  # rows pick input columns 3, 1, 7
+    assert np.array_equal(numpy_ref.linear(x, perm), x[:, [3, 1, 7]])
+    x2 = r.standard_normal((5, 8))
+    assert np.allclose(numpy_ref.linear(2 * x + x2, w), 2 * y + numpy_ref.linear(x2, w), atol=1e-12)
+    assert numpy_ref.linear(x, w).shape == (5, 3)
