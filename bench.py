@@ -16,7 +16,7 @@ kernel in every timed step), the same figure for the whole layer call, and the f
 oracle timed on a bounded sample of the same workload.
 
     --extras                also time state capture/restore, a 370-row fork, decode steps
-                            of 1 and 32 sessions and the two projections
+                            of 1 and 32 sessions, the two projections and the attention layer
     --copy-calibration N    run a plain N-byte device copy after timing (for counter scaling)
 """
 import argparse
@@ -116,7 +116,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", action="store_true",
                     help="also time state capture/restore, a 370-row fork, decode "
-                         "steps of 1 and 32 sessions and the two projections")
+                         "steps of 1 and 32 sessions, the two projections and the full-attention "
+                         "layer")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run a plain device copy of BYTES bytes three "
                          "times (reference dispatch for the HBM byte counters)")
@@ -263,6 +264,32 @@ def main():
                                         "tflops": round(tflops, 1),
                                         "mfma_bf16_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
             del px, pw, py
+
+        # the hybrid's full-attention layer at the same length: 16 query heads over 2 key
+        # heads of width 256, causal over 8,192 rows (flops: QK^T and PV over the causal
+        # triangle, 4 D per query-key pair)
+        Hq_a, Hkv_a, D_a = 16, 2, 256
+        aq = torch.randn((T_ROWS, Hq_a, D_a), device=dev).to(torch.bfloat16)
+        ak = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
+        av = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
+        ao = torch.empty_like(aq)
+        adesc = b.make_attn_desc(Hq_a, Hkv_a, D_a)
+        for _ in range(2):
+            b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)])
+        reps5 = 10
+        e2.record(stream)
+        for _ in range(reps5):
+            b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)])
+        e3.record(stream)
+        torch.cuda.synchronize()
+        att_ms = e2.elapsed_time(e3) / reps5
+        att_flops = 4.0 * D_a * Hq_a * T_ROWS * (T_ROWS + 1) / 2
+        att_tf = att_flops / (att_ms * 1e-3) / 1e12
+        extras["attention_prefill"] = {"T": T_ROWS, "n_q_heads": Hq_a, "n_kv_heads": Hkv_a,
+                                       "head_dim": D_a, "us": round(att_ms * 1e3, 1),
+                                       "tflops": round(att_tf, 1),
+                                       "mfma_bf16_frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        del aq, ak, av, ao
 
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters

@@ -59,6 +59,21 @@ class gdn_state(ctypes.Structure):
                 ("tag", ctypes.c_uint64)]
 
 
+class gdn_attn_desc(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+    @property
+    def out_torch(self):
+        return _CODE_DTYPE[self.out_dtype]
+
+
+class gdn_attn_seq(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("o", ctypes.c_void_p), ("pos0", ctypes.c_int64), ("T", ctypes.c_int64)]
+
+
 class gdn_ckpt_ring(ctypes.Structure):
     _fields_ = [("cap", ctypes.c_int32), ("n", ctypes.c_int32),
                 ("pos", ctypes.c_int64 * MAX_CHECKPOINTS),
@@ -99,6 +114,8 @@ def _load():
         "gdn_state_save": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
         "gdn_state_load": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
         "gdn_linear": (I32, [I64, I32, I32, V, V, V, I32, V]),
+        "gdn_attention_prefill": (I32, [ctypes.POINTER(gdn_attn_desc), I32,
+                                        ctypes.POINTER(gdn_attn_seq), V]),
         "gdn_commit_rows": (I64, [I64, I32]),
         "gdn_shared_prefix_rows": (I64, [I64, I64]),
         "gdn_ckpt_init": (I32, [R, I32]),
@@ -340,6 +357,20 @@ def gdn_linear(x, w, y, stream=None):
     N = w.shape[0]
     _check(lib.gdn_linear(int(T), int(K), int(N), _ptr(x), _ptr(w), _ptr(y),
                           _DTYPE_CODE[y.dtype], _stream(stream)), "gdn_linear")
+
+
+def make_attn_desc(n_q_heads, n_kv_heads, head_dim, *, out_dtype=torch.bfloat16, scale=None):
+    return gdn_attn_desc(n_q_heads, n_kv_heads, head_dim, _DTYPE_CODE[out_dtype],
+                         float(head_dim ** -0.5 if scale is None else scale))
+
+
+def gdn_attention_prefill(desc, seqs, stream=None):
+    """seqs: list of (q [T][Hq][D], k cache [>= pos0+T][Hkv][D], v cache, o [T][Hq][D], pos0)."""
+    arr = (gdn_attn_seq * max(1, len(seqs)))()
+    for i, (q, k, v, o, pos0) in enumerate(seqs):
+        arr[i] = gdn_attn_seq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), int(pos0), int(q.shape[0]))
+    _check(lib.gdn_attention_prefill(ctypes.byref(desc), len(seqs), arr, _stream(stream)),
+           "gdn_attention_prefill")
 
 
 def gdn_commit_rows(n, grid):

@@ -1,0 +1,356 @@
+// gdn_attention.hip -- causal prefill attention for the full-attention layers of a hybrid model:
+// bf16 q / K / V, fp32 softmax and accumulation, on gfx950 MFMA.
+//
+// The pages run these layers as split-K flash attention: key positions are cut into splits of
+// 256, the softmax is kept online, and the splits are merged in an order fixed by absolute
+// position alone, so that any way of cutting a prompt into calls (or of grouping branches)
+// gives the same bits ("Long context and sessions", section "The KV cache").  Here each query
+// row folds its splits into a running (max, sum, accumulator) in ascending split order, one
+// split per update: the split's largest score joins the running max, the running sum and
+// accumulator are rescaled by exp(old max - new max), and the split's exponentials, rounded to
+// bf16, are added with their value rows.  Split boundaries are absolute multiples of 256 and
+// every row's arithmetic is the same whichever call, tile or lane it lands in.  Keys past a
+// row's own position are masked to an exact zero weight; a 64-key block that is masked for
+// every row of a workgroup is skipped, which changes nothing (x + 0 and x * 1 are exact).
+//
+// Workgroup: 8 waves, each owning 16 query rows of one query head; the waves share the key
+// head, so one 64-key block of K or V staged in LDS serves all of them.  For each split the
+// waves first form S^T = K Q^T for its 256 keys (16 x 256 scores per wave, in registers), then
+// the softmax update, then O^T += V^T P^T.  Both products put a query row in lane % 16, so the
+// row statistics and the rescaling stay inside a lane.  K and V blocks stream through a ring
+// of three LDS slots, loaded two blocks ahead.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gdn_internal.h"
+
+namespace gdn {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kSplit = 256;  // key positions per split
+constexpr int kBlk = 64;     // keys per LDS block
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 3;
+
+// An LDS block holds 64 key rows of D bf16, each row padded by one 16-byte chunk: chunk c of
+// row t sits at 16-byte slot t (D / 8 + 1) + c, so rows t and t + 1 start one chunk apart
+// (mod the 256-byte bank window) and every fragment address is one per-lane base plus a
+// compile-time offset.
+template <int D>
+constexpr int kRowChunks = D / 8 + 1;
+template <int D>
+constexpr int kSlotChunks = kBlk * kRowChunks<D>;
+
+// Key order inside a 16-key MFMA tile: row r of the tile is key sigma(r) = 2 (r mod 8) + r / 8.
+// With it the 16 rows of a K fragment read have distinct residues mod 16 (no bank conflict),
+// and the 8 rows each half-wave touches in a transposed V read are all even or all odd, so
+// together with the two chunks per row they also fill 16 distinct slots.
+__device__ __forceinline__ int sigma(int r) { return ((r & 7) << 1) | (r >> 3); }
+
+// One 64-key block (keys key0 .. key0 + 63 of key head kvh) of a [rows][Hkv][D] cache into
+// registers; keys at or past L read as zero.
+template <int D>
+__device__ __forceinline__ void blk_load(const uint16_t *base, int64_t key0, int64_t L, int Hkv,
+                                         int kvh, int tid, u32x4 (&v)[D / 64])
+{
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+        const int id = tid + kThreads * i, row = id / (D / 8), pc = id % (D / 8);
+        const int64_t key = key0 + row;
+        v[i] = key < L ? *(const u32x4 *)(base + (key * Hkv + kvh) * D + 8 * pc)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void blk_store(u32x4 *slot, int tid, const u32x4 (&v)[D / 64])
+{
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {
+        const int id = tid + kThreads * i, row = id / (D / 8), pc = id % (D / 8);
+        slot[row * kRowChunks<D> + pc] = v[i];
+    }
+}
+
+// K fragment (A operand of S^T = K Q^T) for tile q4 and d-step ks: lane (r = lane % 16, g)
+// holds K[16 q4 + sigma(r)][32 ks + 8 g .. + 7].  kbase = the lane's slot offset of
+// (sigma(r), g).
+template <int D>
+__device__ __forceinline__ bf16x8 k_frag(const u32x4 *slot, int kbase, int q4, int ks)
+{
+    return __builtin_bit_cast(bf16x8, slot[kbase + 16 * q4 * kRowChunks<D> + 4 * ks]);
+}
+
+// V^T fragment (A operand of O^T = V^T P^T) for output columns 16 ct .. + 15 and the 32 keys
+// of tiles 2 kb, 2 kb + 1 of a block: lane (col m = lane % 16, g) holds V[key][16 ct + m] for
+// the keys 32 kb + sigma(4 g + e) and 32 kb + 16 + sigma(4 g + e), e = 0..3, the keys whose
+// softmax weights the lane holds in the S^T layout.  ds_read_b64_tr_b16 gives output lane i of a
+// 16-lane group element i % 4 of the 8-byte reads of lanes 4 e + i / 4 (e = 0..3); lane 4 a + b
+// reads columns 16 ct + 4 b .. + 3 of key row 32 kb + sigma(4 g + a), so output lane i gets
+// column 16 ct + i of those four rows.  vbase = the lane's byte offset for ct = kb = 0.
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const u32x4 *slot, int vbase, int ct, int kb)
+{
+    typedef __attribute__((address_space(3))) short4_t lds_short4;
+    const char *b = (const char *)slot + vbase + 32 * ct + 512 * kb * kRowChunks<D>;
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)b);
+    const short4_t hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(b + 256 * kRowChunks<D>));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <typename Out>
+__device__ __forceinline__ void store4(Out *p, f32x4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float *p, f32x4 v)
+{
+    *(f32x4 *)p = v;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v)
+{
+    const bf16x4 h = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *(u32x2 *)p = __builtin_bit_cast(u32x2, h);
+}
+
+// The next block to stage: (split j, V or K, block k within the split).
+struct Cursor {
+    int j, isv, k;
+};
+
+__device__ __forceinline__ void advance(Cursor &c, int ns, int nk_last)
+{
+    const int nk = c.j == ns - 1 ? nk_last : kSplit / kBlk;
+    if (++c.k == nk) {
+        c.k = 0;
+        if (c.isv) {
+            c.isv = 0;
+            ++c.j;
+        } else {
+            c.isv = 1;
+        }
+    }
+}
+
+template <int D, typename Out>
+__global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int Hkv, int HW,
+                                                        float c2)
+{
+    __shared__ u32x4 ring[kRing][kSlotChunks<D>];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, g = lane >> 4;
+    const int RW = kWaves / HW;  // 16-row tiles per workgroup
+    const int R = Hq / Hkv;
+
+    // heavier (later) row tiles first; within a tile the head groups are adjacent, so that
+    // consecutive workgroups (which go to different XCDs) take different key heads
+    const int n_groups = Hkv * (Hq / Hkv / HW);
+    const int group = (int)blockIdx.x % n_groups;
+    const int tile = (int)(gridDim.x / n_groups) - 1 - (int)blockIdx.x / n_groups;
+    int s = 0;
+    for (int i = 1; i < a.n; ++i)
+        if (a.seq[i].tile0 <= tile) s = i;
+    const AttnSeq &sq = a.seq[s];
+    const int64_t T = sq.T, pos0 = sq.pos0, L = pos0 + T;
+    const int64_t t0 = (int64_t)(tile - sq.tile0) * 16 * RW;
+    const int groups_per_kv = R / HW;
+    const int kvh = group / groups_per_kv;
+    const int h = kvh * R + (group % groups_per_kv) * HW + wave % HW;
+    const int64_t tw = t0 + 16 * (wave / HW);  // this wave's first row
+    const int64_t t_end = t0 + 16 * RW < T ? t0 + 16 * RW : T;
+    const int64_t p_last = pos0 + t_end - 1;   // last valid row of the workgroup
+    const int ns = (int)(p_last / kSplit) + 1;
+    const int nk_last = (int)((p_last % kSplit) / kBlk) + 1;
+    const int64_t trow = tw + li, prow = pos0 + trow;
+
+    const uint16_t *kp = (const uint16_t *)sq.k, *vp = (const uint16_t *)sq.v;
+    const int kbase = sigma(li) * kRowChunks<D> + g;
+    const int j4 = lane & 15;
+    const int vbase = 16 * sigma(4 * g + j4 / 4) * kRowChunks<D> + 8 * (j4 % 4);
+
+    // q fragments of this lane's row (zero past T): B operand, lane (row, g) holds d 32 ks + 8 g ..
+    bf16x8 qf[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+        qf[ks] = trow < T ? __builtin_bit_cast(
+                                bf16x8, *(const u32x4 *)((const uint16_t *)sq.q +
+                                                         (trow * Hq + h) * D + 32 * ks + 8 * g))
+                          : bf16x8{};
+
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -__builtin_inff(), l = 0.f;
+
+    // prologue: blocks 0 and 1 into slots 0 and 1
+    Cursor ld = {0, 0, 0};
+    u32x4 stage[D / 64];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        if (ld.j < ns) {
+            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, kvh, tid,
+                        stage);
+            blk_store<D>(ring[b], tid, stage);
+            advance(ld, ns, nk_last);
+        }
+    }
+    __syncthreads();
+    int rs = 0;
+
+    // One block step: stage the block two ahead, run `work` on slot rs, store, barrier.
+    auto step = [&](auto &&work) {
+        const bool more = ld.j < ns;
+        if (more)
+            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, kvh, tid,
+                        stage);
+        work(ring[rs]);
+        if (more) {
+            blk_store<D>(ring[rs == 0 ? 2 : rs - 1], tid, stage);
+            advance(ld, ns, nk_last);
+        }
+        __syncthreads();
+        rs = rs == kRing - 1 ? 0 : rs + 1;
+    };
+
+    for (int j = 0; j < ns; ++j) {
+        const int nk = j == ns - 1 ? nk_last : kSplit / kBlk;
+        f32x4 S[kSplit / 16];  // S^T tiles: lane (row li, g) holds keys 16 kt + sigma(4 g + i)
+#pragma unroll
+        for (int kc = 0; kc < kSplit / kBlk; ++kc) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) S[4 * kc + q4] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (kc < nk)
+                step([&](const u32x4 *slot) {
+                    // fragments of d-step ks + 1 are read while step ks multiplies
+                    bf16x8 kf[2][4];
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) kf[0][q4] = k_frag<D>(slot, kbase, q4, 0);
+#pragma unroll
+                    for (int ks = 0; ks < D / 32; ++ks) {
+                        if (ks + 1 < D / 32)
+#pragma unroll
+                            for (int q4 = 0; q4 < 4; ++q4)
+                                kf[(ks + 1) & 1][q4] = k_frag<D>(slot, kbase, q4, ks + 1);
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            S[4 * kc + q4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                kf[ks & 1][q4], qf[ks], S[4 * kc + q4], 0, 0, 0);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                });
+        }
+
+        // softmax update for split j (scores in units of log2: s * c2).  Key 16 kt + sigma(4 g
+        // + i) of the split is live for this row when it is at most lim: not past the row's
+        // own position, and inside a staged block.
+        const int64_t key_base = (int64_t)kSplit * j;
+        const int64_t rel = prow - key_base;
+        const int lim = rel < kBlk * nk - 1 ? (int)rel : kBlk * nk - 1;
+        int sg[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sg[i] = sigma(4 * g + i);
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int kt = 0; kt < kSplit / 16; ++kt) {
+            const int lk = lim - 16 * kt;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (sg[i] > lk) S[kt][i] = -__builtin_inff();
+                mx = fmaxf(mx, S[kt][i]);
+            }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m, mx * c2);
+        const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+        m = m_new;
+        l *= alpha;
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct) acc[ct] *= alpha;
+
+        // weights of the 32 keys 32 kb .. in the lane's key order, rounded to bf16; the row sum
+        // takes the rounded values
+        auto weights = [&](int kb) {
+            bf16x8 pk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sv = S[2 * kb + e / 4][e % 4];
+                const float p = sv == -__builtin_inff()
+                                    ? 0.f
+                                    : __builtin_amdgcn_exp2f(fmaf(sv, c2, -m_new));
+                pk[e] = (__bf16)p;
+                l += (float)pk[e];
+            }
+            return pk;
+        };
+#pragma unroll
+        for (int vc = 0; vc < kSplit / kBlk; ++vc) {
+            if (vc < nk)
+                step([&](const u32x4 *slot) {
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 2; ++kb2) {
+                        const bf16x8 pk = weights(2 * vc + kb2);
+                        // V^T fragments of columns ct + 1 .. ct + 2 in flight while ct multiplies
+                        bf16x8 vf[4];
+                        vf[0] = v_frag<D>(slot, vbase, 0, kb2);
+                        vf[1] = v_frag<D>(slot, vbase, 1, kb2);
+#pragma unroll
+                        for (int ct = 0; ct < D / 16; ++ct) {
+                            if (ct + 2 < D / 16) vf[(ct + 2) & 3] = v_frag<D>(slot, vbase, ct + 2, kb2);
+                            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct & 3], pk,
+                                                                             acc[ct], 0, 0, 0);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                });
+        }
+    }
+
+    // the row's sum from the four lanes that hold it (the same bits in all four)
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (trow < T) {
+        const float inv = 1.0f / l;
+        Out *orow = (Out *)sq.o + (trow * Hq + h) * D;
+#pragma unroll
+        for (int ct = 0; ct < D / 16; ++ct) store4<Out>(orow + 16 * ct + 4 * g, acc[ct] * inv);
+    }
+}
+
+template <int D>
+int launch_d(const AttnArgs &aa, int n_tiles, int Hq, int Hkv, int HW, float c2, int out_dtype,
+             hipStream_t st)
+{
+    const dim3 grid((unsigned)(n_tiles * Hkv * (Hq / Hkv / HW)));
+    if (out_dtype == GDN_BF16)
+        hipLaunchKernelGGL((attn_kernel<D, uint16_t>), grid, dim3(kThreads), 0, st, aa, Hq, Hkv,
+                           HW, c2);
+    else
+        hipLaunchKernelGGL((attn_kernel<D, float>), grid, dim3(kThreads), 0, st, aa, Hq, Hkv, HW,
+                           c2);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+
+int launch_attention(const AttnArgs &aa, int n_tiles, int Hq, int Hkv, int D, int HW, float c2,
+                     int out_dtype, void *stream)
+{
+    (void)hipGetLastError();
+    if (n_tiles == 0) return 0;
+    hipStream_t st = (hipStream_t)stream;
+    return D == 128 ? launch_d<128>(aa, n_tiles, Hq, Hkv, HW, c2, out_dtype, st)
+                    : launch_d<256>(aa, n_tiles, Hq, Hkv, HW, c2, out_dtype, st);
+}
+
+}  // namespace gdn

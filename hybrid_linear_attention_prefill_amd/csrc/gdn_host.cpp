@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cerrno>
+#include <cmath>
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
@@ -685,6 +686,75 @@ gdn_status gdn_linear(int64_t T, int32_t K, int32_t N, const void *x, const void
     if (T == 0) return GDN_OK;
     if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return GDN_EINVAL;
     if (launch_linear(T, K, N, x, w, y, out_dtype, stream) != 0) return GDN_EDEVICE;
+    return GDN_OK;
+}
+
+static bool ranges_overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+gdn_status gdn_attention_prefill(const gdn_attn_desc *desc, int32_t B, const gdn_attn_seq *seqs,
+                                 void *stream)
+{
+    if (!desc || B < 0 || (B > 0 && !seqs)) return GDN_EINVAL;
+    const gdn_attn_desc &d = *desc;
+    if (d.out_dtype != GDN_BF16 && d.out_dtype != GDN_F32) return GDN_EINVAL;
+    if (!(d.scale > 0.f) || !std::isfinite(d.scale)) return GDN_EINVAL;
+    if (d.n_q_heads <= 0 || d.n_kv_heads <= 0 || d.n_q_heads % d.n_kv_heads != 0) return GDN_ESHAPE;
+    const int R = d.n_q_heads / d.n_kv_heads;
+    if (!(R == 1 || R == 2 || R == 4 || R % 8 == 0)) return GDN_ESHAPE;
+    if (d.head_dim != 128 && d.head_dim != 256) return GDN_ESHAPE;
+    const int HW = attn_heads_per_wg(d.n_q_heads, d.n_kv_heads);
+    const int64_t rows_per_tile = 16 * (8 / HW);
+    const int64_t n_groups = (int64_t)d.n_kv_heads * (R / HW);
+    const size_t out_el = d.out_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t qrow = (int64_t)d.n_q_heads * d.head_dim, kvrow = (int64_t)d.n_kv_heads * d.head_dim;
+    for (int32_t i = 0; i < B; ++i) {
+        const gdn_attn_seq &q = seqs[i];
+        if (q.T < 0 || q.pos0 < 0 || q.T > ((int64_t)1 << 40) || q.pos0 > ((int64_t)1 << 40))
+            return GDN_EINVAL;
+        if (q.T == 0) continue;
+        if (!q.q || !q.k || !q.v || !q.o) return GDN_EINVAL;
+        if (!aligned(q.q, 16) || !aligned(q.k, 16) || !aligned(q.v, 16) || !aligned(q.o, 16))
+            return GDN_EINVAL;
+        if (((q.T + rows_per_tile - 1) / rows_per_tile) * n_groups > INT32_MAX) return GDN_EINVAL;
+        const size_t ob = (size_t)(q.T * qrow) * out_el, qb = (size_t)(q.T * qrow) * 2;
+        const size_t kb = (size_t)((q.pos0 + q.T) * kvrow) * 2;
+        if (ranges_overlap(q.o, ob, q.q, qb) || ranges_overlap(q.o, ob, q.k, kb) ||
+            ranges_overlap(q.o, ob, q.v, kb))
+            return GDN_EALIAS;
+    }
+    const float c2 = d.scale * 1.4426950408889634f;  // scores in units of log2
+    AttnArgs aa;
+    aa.n = 0;
+    int64_t tiles = 0;
+    auto flush = [&]() -> int {
+        if (aa.n == 0) return 0;
+        const int r = launch_attention(aa, (int)tiles, d.n_q_heads, d.n_kv_heads, d.head_dim, HW,
+                                       c2, d.out_dtype, stream);
+        aa.n = 0;
+        tiles = 0;
+        return r;
+    };
+    for (int32_t i = 0; i < B; ++i) {
+        const gdn_attn_seq &q = seqs[i];
+        if (q.T == 0) continue;
+        const int64_t nt = (q.T + rows_per_tile - 1) / rows_per_tile;
+        if (aa.n == kMaxSegPerLaunch || (tiles + nt) * n_groups > INT32_MAX)
+            if (flush() != 0) return GDN_EDEVICE;
+        AttnSeq &s = aa.seq[aa.n++];
+        s.q = q.q;
+        s.k = q.k;
+        s.v = q.v;
+        s.o = q.o;
+        s.pos0 = q.pos0;
+        s.T = q.T;
+        s.tile0 = (int32_t)tiles;
+        tiles += nt;
+    }
+    if (flush() != 0) return GDN_EDEVICE;
     return GDN_OK;
 }
 

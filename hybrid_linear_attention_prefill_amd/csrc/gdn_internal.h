@@ -68,6 +68,26 @@ struct DecodeArgs {
     DecodeSeq seq[kMaxSegPerLaunch];
 };
 
+// One sequence of an attention launch (device pointers): query rows pos0 .. pos0 + T - 1, keys
+// and values 0 .. pos0 + T - 1 of its caches.  tile0 is its first row tile in the launch.
+struct AttnSeq {
+    const void *q;  // [T][Hq][D]
+    const void *k;  // [pos0 + T][Hkv][D]
+    const void *v;  // [pos0 + T][Hkv][D]
+    void *o;        // [T][Hq][D]
+    int64_t pos0, T;
+    int32_t tile0;
+};
+
+struct AttnArgs {
+    int32_t n;
+    AttnSeq seq[kMaxSegPerLaunch];
+};
+
+// Query heads and 16-row tiles one attention workgroup covers: HW heads of one key head, each
+// over 8 / HW row tiles (HW = min(Hq / Hkv, 8)).
+inline int attn_heads_per_wg(int Hq, int Hkv) { return Hq / Hkv < 8 ? Hq / Hkv : 8; }
+
 size_t workspace_bytes(const gdn_desc &d, int64_t n_sub);
 Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base);
 
@@ -85,6 +105,9 @@ int launch_conv_step(const gdn_desc &d, const void *x, const void *conv_w, void 
 // y[T][N] = x[T][K] w[N][K]^T, bf16 in, fp32 accumulation, y in out_dtype (gdn_linear.hip).
 int launch_linear(int64_t T, int K, int N, const void *x, const void *w, void *y, int out_dtype,
                   void *stream);
+// Causal attention of aa.n sequences; c2 = scale * log2(e) (gdn_attention.hip).
+int launch_attention(const AttnArgs &aa, int n_tiles, int Hq, int Hkv, int D, int HW, float c2,
+                     int out_dtype, void *stream);
 int launch_zero(void *p, size_t bytes, void *stream);
 int launch_copy(void *dst, const void *src, size_t bytes, void *stream);
 

@@ -8,7 +8,8 @@ Draws use numpy's PCG64 seeded with ``[seed, stream]``; the stream ids are fixed
 
   0 q channels | 1 k channels | 2 v channels / embedding table | 3 beta logits |
   4 g logits | 5 conv weights | 6 token ids | 7 turn cuts | 8 question ids |
-  9 branch lengths | 10 divergence point | 11 projection inputs | 12 projection weights
+  9 branch lengths | 10 divergence point | 11 projection inputs | 12 projection weights |
+  13 attention queries | 14 attention keys | 15 attention values
 
 Value recipes (the pages print no data; these are stated stand-ins):
   x ~ N(0,1) cast to the activation dtype with round-to-nearest-even;
@@ -23,6 +24,7 @@ import torch
 STREAM_Q, STREAM_K, STREAM_V, STREAM_BETA, STREAM_G, STREAM_W = 0, 1, 2, 3, 4, 5
 STREAM_IDS, STREAM_CUTS, STREAM_QUESTION, STREAM_BRANCH, STREAM_DIVERGE = 6, 7, 8, 9, 10
 STREAM_PROJ_X, STREAM_PROJ_W = 11, 12
+STREAM_ATT_Q, STREAM_ATT_K, STREAM_ATT_V = 13, 14, 15
 
 
 @dataclass(frozen=True)
@@ -150,3 +152,17 @@ def linear_inputs(T, K, N, seed=0):
     x = cast(rng(seed, STREAM_PROJ_X).standard_normal((T, K)), torch.bfloat16)
     w = cast(rng(seed, STREAM_PROJ_W).standard_normal((N, K)) / np.sqrt(K), torch.bfloat16)
     return x, w
+
+
+def attention_inputs(T, Hq, Hkv, D, seed=0):
+    """Queries [T, Hq, D] and key / value caches [T, Hkv, D] for T positions, bf16.  q and k are
+    N(0, 1) with a per-head scale drawn from [0.5, 2) (so that some heads attend sharply and
+    others broadly at the usual 1/sqrt(D) score scale); v is N(0, 1)."""
+    r = rng(seed, STREAM_ATT_Q)
+    qs = 0.5 + 1.5 * r.random((1, Hq, 1))
+    q = cast(r.standard_normal((T, Hq, D)) * qs, torch.bfloat16)
+    r = rng(seed, STREAM_ATT_K)
+    ks = 0.5 + 1.5 * r.random((1, Hkv, 1))
+    k = cast(r.standard_normal((T, Hkv, D)) * ks, torch.bfloat16)
+    v = cast(rng(seed, STREAM_ATT_V).standard_normal((T, Hkv, D)), torch.bfloat16)
+    return q, k, v

@@ -267,6 +267,44 @@ gdn_status gdn_decode_step(const gdn_desc *desc, int32_t B, const void *x, const
 gdn_status gdn_linear(int64_t T, int32_t K, int32_t N, const void *x, const void *w, void *y,
                       int32_t out_dtype, void *stream);
 
+/* ---------------------------------------------------------------- full-attention layers */
+
+/* The hybrid's full-attention layers: causal softmax attention of a call's query rows over the
+ * key/value cache, with grouped key heads. */
+typedef struct {
+    int32_t n_q_heads, n_kv_heads; /* n_q_heads % n_kv_heads == 0; the ratio is 1, 2, 4 or a
+                                      multiple of 8 */
+    int32_t head_dim;              /* 128 or 256 */
+    int32_t out_dtype;             /* GDN_BF16 or GDN_F32 */
+    float scale;                   /* score scale (finite, > 0), usually head_dim^-1/2 */
+} gdn_attn_desc;
+
+typedef struct {
+    const void *q; /* [T][n_q_heads][head_dim] bf16: the call's query rows */
+    const void *k; /* [pos0 + T][n_kv_heads][head_dim] bf16: the key cache, the call's own
+                      rows already appended; rows past pos0 + T are never read */
+    const void *v; /* the value cache, laid out like k */
+    void *o;       /* [T][n_q_heads][head_dim] out_dtype; must not overlap q, k or v */
+    int64_t pos0;  /* absolute position of q's first row (rows 0 .. pos0 - 1 are cached) */
+    int64_t T;     /* query rows of the call (0: nothing to do) */
+} gdn_attn_seq;
+
+/* o = softmax(scale q K^T, keys 0 .. p for the query at absolute position p) V for every row of
+ * every sequence, query head h reading key head h / (n_q_heads / n_kv_heads).  Split-K flash
+ * attention as the pages run it ("Long context and sessions", section "The KV cache"): key
+ * positions in splits of 256 at absolute multiples of 256, an online softmax that folds the
+ * splits into a running max, sum and accumulator in ascending order, so each output row depends
+ * only on its absolute position and the cache contents: cutting a prompt into calls at any row,
+ * or running branches over a shared cached prefix, gives the same bits as one call over the
+ * whole prompt.  Rewinding needs no checkpoint: a later call from any pos0 reuses cache rows
+ * below pos0 as they are ("The shadow reader", section "Exact on a grid").  fp32 scores,
+ * softmax and accumulation; the softmax weights meet V as bf16.  All pointers device, 16-byte
+ * aligned.  B >= 0 sequences (an array on the host), cut into launches of at most 32.
+ * Asynchronous on `stream`.  GDN_EINVAL / GDN_ESHAPE / GDN_EALIAS on bad arguments, nothing
+ * enqueued. */
+gdn_status gdn_attention_prefill(const gdn_attn_desc *desc, int32_t B, const gdn_attn_seq *seqs,
+                                 void *stream);
+
 /* ---------------------------------------------------------------- host scheduling (no device) */
 
 /* Rows a COMMIT from an aligned position absorbs out of n available rows:

@@ -101,3 +101,29 @@ def linear(x, w):
     x = np.asarray(x, np.float64)
     w = np.asarray(w, np.float64)
     return x @ w.T
+
+
+def attention(q, k, v, pos0, scale):
+    """Causal softmax attention of the full-attention layers, in float64: the query at absolute
+    position p = pos0 + t attends to keys 0 .. p, and query head h reads key head
+    h // (Hq / Hkv).  o[t, h] = sum_j softmax_j(scale q[t, h] . k[j, h']) v[j, h'].  The pages
+    compute it as split-K flash attention with an online softmax ("Long context and sessions",
+    section "The KV cache"); rescaling by a running max changes only rounding, so the exact
+    result is the plain definition written here.
+
+    q [T, Hq, D]; k, v [>= pos0 + T, Hkv, D]; returns o [T, Hq, D]."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    R = Hq // Hkv
+    o = np.zeros((T, Hq, D))
+    for h in range(Hq):
+        kh, vh = k[:, h // R, :], v[:, h // R, :]
+        for t in range(T):
+            n = pos0 + t + 1
+            s = scale * (kh[:n] @ q[t, h])
+            w = np.exp(s - s.max())
+            o[t, h] = (w / w.sum()) @ vh[:n]
+    return o

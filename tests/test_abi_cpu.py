@@ -283,3 +283,31 @@ def test_checkpoint_ring_matches_brute_force():
 def test_status_strings():
     for code in (0, -1, -2, -3, -4, -5, -6, -7, -99):
         assert isinstance(b.gdn_status_str(code), str) and b.gdn_status_str(code)
+
+
+def test_attention_validation():
+    def call(Hq=8, Hkv=1, D=128, od=b.GDN_BF16, scale=0.1, seqs=None, B=None):
+        d = b.gdn_attn_desc(Hq, Hkv, D, od, scale)
+        if seqs is None:
+            seqs = [b.gdn_attn_seq(FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (3 << 20), 0, 16)]
+        arr = (b.gdn_attn_seq * max(1, len(seqs)))(*seqs)
+        return b.lib.gdn_attention_prefill(b.ctypes.byref(d), len(seqs) if B is None else B,
+                                           arr, None)
+
+    for kw in (dict(Hq=6, Hkv=4), dict(Hq=12, Hkv=4), dict(Hq=0), dict(D=64), dict(D=192)):
+        assert call(**kw) == b.GDN_ESHAPE, kw
+    for kw in (dict(od=7), dict(scale=0.0), dict(scale=float("inf")), dict(scale=float("nan")),
+               dict(B=-1)):
+        assert call(**kw) == b.GDN_EINVAL, kw
+    S = b.gdn_attn_seq
+    bad = [S(None, FAKE, FAKE, FAKE, 0, 4), S(FAKE + 8, FAKE, FAKE, FAKE, 0, 4),
+           S(FAKE, FAKE, FAKE, FAKE, -1, 4), S(FAKE, FAKE, FAKE, FAKE, 0, -2)]
+    for s in bad:
+        assert call(seqs=[s]) == b.GDN_EINVAL
+    # o overlapping q or the caches
+    assert call(seqs=[S(FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + 256, 0, 16)]) == b.GDN_EALIAS
+    assert call(seqs=[S(FAKE, FAKE + (1 << 20), FAKE + (2 << 20), FAKE + (2 << 20) + 512, 0, 16)]) \
+        == b.GDN_EALIAS
+    # nothing to do: empty sequences are fine with any pointers
+    assert call(seqs=[S(None, None, None, None, 5, 0)]) == b.GDN_OK
+    assert call(seqs=[], B=0) == b.GDN_OK

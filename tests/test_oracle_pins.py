@@ -398,3 +398,66 @@ def test_linear_against_brute_force_and_closed_forms():
     x2 = r.standard_normal((5, 8))
     assert np.allclose(numpy_ref.linear(2 * x + x2, w), 2 * y + numpy_ref.linear(x2, w), atol=1e-12)
     assert numpy_ref.linear(x, w).shape == (5, 3)
+
+
+def test_attention_against_brute_force_loops():
+    """Explicit loops with math.exp on a tiny case with grouped heads and cached rows."""
+    import math
+    from oracle import numpy_ref
+    r = np.random.default_rng(11)
+    T, Hq, Hkv, D, pos0 = 3, 4, 2, 5, 2
+    q = r.standard_normal((T, Hq, D))
+    k = r.standard_normal((pos0 + T, Hkv, D))
+    v = r.standard_normal((pos0 + T, Hkv, D))
+    scale = 0.37
+    o = numpy_ref.attention(q, k, v, pos0, scale)
+    for t in range(T):
+        for h in range(Hq):
+            kv = h // (Hq // Hkv)
+            w = []
+            for j in range(pos0 + t + 1):
+                w.append(math.exp(scale * sum(q[t, h, d] * k[j, kv, d] for d in range(D))))
+            for d in range(D):
+                ref = sum(w[j] * v[j, kv, d] for j in range(len(w))) / sum(w)
+                assert abs(o[t, h, d] - ref) < 1e-12
+
+
+def test_attention_closed_forms():
+    """The first position sees only itself; a zero query averages the values it can see; a key
+    far ahead of the others in score takes all the weight; heads read key head h // ratio."""
+    from oracle import numpy_ref
+    r = np.random.default_rng(12)
+    T, Hq, Hkv, D = 6, 4, 2, 8
+    q = r.standard_normal((T, Hq, D))
+    k = r.standard_normal((T, Hkv, D))
+    v = r.standard_normal((T, Hkv, D))
+    o = numpy_ref.attention(q, k, v, 0, 0.3)
+    for h in range(Hq):
+        assert np.array_equal(o[0, h], v[0, h // 2])
+    oz = numpy_ref.attention(np.zeros_like(q), k, v, 0, 0.3)
+    for t in range(T):
+        assert np.allclose(oz[t, 0], v[:t + 1, 0].mean(axis=0), atol=1e-14)
+        assert np.allclose(oz[t, 3], v[:t + 1, 1].mean(axis=0), atol=1e-14)
+    k2 = k.copy()
+    k2[2, 0] = 50.0 * q[5, 1] / np.linalg.norm(q[5, 1])  # head 1 reads key head 0
+    o2 = numpy_ref.attention(q, k2, v, 0, 1.0)
+    assert np.allclose(o2[5, 1], v[2, 0], atol=1e-9)
+    # grouped heads: each query head alone against its own key head
+    for h in range(Hq):
+        alone = numpy_ref.attention(q[:, h:h + 1], k[:, h // 2:h // 2 + 1], v[:, h // 2:h // 2 + 1],
+                                    0, 0.3)
+        assert np.allclose(alone[:, 0], o[:, h], atol=1e-14)
+
+
+def test_attention_continuation_from_cached_rows():
+    """Rows a .. T-1 run from position a over the same cache equal those rows of one pass."""
+    from oracle import numpy_ref
+    r = np.random.default_rng(13)
+    T, D = 9, 4
+    q = r.standard_normal((T, 2, D))
+    k = r.standard_normal((T, 1, D))
+    v = r.standard_normal((T, 1, D))
+    full = numpy_ref.attention(q, k, v, 0, 0.5)
+    for a in (1, 4, 8):
+        part = numpy_ref.attention(q[a:], k, v, a, 0.5)
+        assert np.allclose(part, full[a:], atol=1e-14)
