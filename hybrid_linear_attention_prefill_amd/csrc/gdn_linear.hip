@@ -9,10 +9,12 @@
 // in the same 32-wide blocks, in the same order, by the same MFMA, whatever the row count, the
 // row's place in its tile or the grid; there is no split-K and no shape-dependent choice.
 //
-// Tile: 128 rows x 128 output columns per workgroup, 4 waves each owning 64 x 64 (4 x 4 MFMA
-// tiles of 16 x 16), K in steps of 64 staged in LDS (double-buffered, one barrier per step).
-// The MFMA computes D = W X^T (16 output columns x 16 rows), so that a lane holds four adjacent
-// output columns of one row and stores them with one 8- or 16-byte store.
+// Tile: 256 rows x 256 output columns per workgroup of 8 waves, each wave owning 128 rows x 64
+// columns (8 x 4 MFMA tiles of 16 x 16).  K advances in steps of 64, double-buffered in LDS; the
+// next step's tiles are copied from global memory straight into LDS (no registers) while the
+// current one is multiplied.  The MFMA computes D = W X^T (16 output columns x 16 rows), so
+// that a lane holds four adjacent output columns of one row and stores them with one 8- or
+// 16-byte store.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -28,10 +30,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 128, BN = 128, BK = 64, CH = BK / 8;  // CH 16-byte chunks per tile row
+constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 8;  // CH 16-byte chunks per tile row
+constexpr int kThreads = 512;
 
-// 16-byte chunk c of row r of an LDS tile: the chunk index is XORed with (r / 2) mod 8, so the
-// 16 rows a fragment read touches (and the rows a store wave writes) spread over all banks.
+// 16-byte chunk c of row r of an LDS tile (rows of 128 bytes): the chunk index is XORed with
+// (r / 2) mod 8, so the 16 rows a fragment read touches spread over all banks.
 __device__ __forceinline__ int chunk_at(int r, int c) { return r * CH + (c ^ ((r >> 1) & 7)); }
 
 __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b)
@@ -53,83 +56,89 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v)
     *(u32x2 *)p = u32x2{bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3])};
 }
 
-// One 128-row x 64-K tile of a row-major [rows][ld] bf16 matrix, rows from r0 (rows at or past
-// `rows` read as zero), into registers: 4 chunks per thread.
-__device__ __forceinline__ void load_tile(const uint16_t *M, int64_t rows, int64_t ld, int64_t r0,
-                                          int k0, int tid, u32x4 (&v)[4])
-{
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int id = tid + 256 * i, r = id / CH, c = id % CH;
-        v[i] = (r0 + r < rows) ? *(const u32x4 *)(M + (r0 + r) * ld + k0 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-    }
-}
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void store_tile(u32x4 *L, int tid, const u32x4 (&v)[4])
+// One 256-row x 64-K tile of a row-major [rows][ld] bf16 matrix, rows from r0, copied from
+// global memory into the LDS tile L by direct-to-LDS loads.  Each wave instruction fills 1 KB of
+// LDS in lane order, so lane i of instruction j fills position p = 64 (4 wave + j) + i, and
+// fetches the chunk that the swizzle puts there.  Rows at or past `rows` repeat the last row:
+// they only feed outputs that are never stored.
+__device__ __forceinline__ void tile_to_lds(const uint16_t *M, int64_t rows, int64_t ld, int64_t r0,
+                                            int k0, u32x4 *L, int wave, int lane)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int id = tid + 256 * i;
-        L[chunk_at(id / CH, id % CH)] = v[i];
+    for (int j = 0; j < 4; ++j) {
+        const int p = 64 * (4 * wave + j) + lane, r = p / CH, c = (p % CH) ^ ((r >> 1) & 7);
+        const int64_t gr = r0 + r < rows ? r0 + r : rows - 1;
+        __builtin_amdgcn_global_load_lds((const void *)(M + gr * ld + k0 + 8 * c),
+                                         (lds_void *)(L + 64 * (4 * wave + j)), 16, 0, 0);
     }
 }
 
 template <typename Out>
-__global__ __launch_bounds__(256) void linear_kernel(const uint16_t *__restrict__ x,
-                                                     const uint16_t *__restrict__ w,
-                                                     Out *__restrict__ y, int64_t T, int K, int N)
+__global__ __launch_bounds__(kThreads) void linear_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ w,
+                                                          Out *__restrict__ y, int64_t T, int K,
+                                                          int N)
 {
-    __shared__ u32x4 Xs[2][BM * CH], Ws[2][BN * CH];
+    // two separate buffers (not one array indexed by parity): the compiler then sees that the
+    // copies into one do not alias the reads of the other, and does not wait for them early
+    __shared__ u32x4 X0[BM * CH], W0[BN * CH], X1[BM * CH], W1[BN * CH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;     // this wave's 64 x 64 quarter
+    const int wm = wave & 1, wn = wave >> 1;  // this wave's 128 x 64 part
     const int64_t m0 = (int64_t)blockIdx.x * BM;
     const int64_t n0 = (int64_t)blockIdx.y * BN;
     const int li = lane % 16, kg = lane / 16;
 
-    f32x4 acc[4][4];  // [output column tile i][row tile j]
+    f32x4 acc[4][8];  // [output column tile i][row tile j]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    u32x4 xv[4], wv[4];
-    load_tile(x, T, K, m0, 0, tid, xv);
-    load_tile(w, N, K, n0, 0, tid, wv);
-    store_tile(Xs[0], tid, xv);
-    store_tile(Ws[0], tid, wv);
-    __syncthreads();
-    const int nk = K / BK;
-    for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nk) {  // the next K step, in flight during this one's MFMAs
-            load_tile(x, T, K, m0, (kt + 1) * BK, tid, xv);
-            load_tile(w, N, K, n0, (kt + 1) * BK, tid, wv);
-        }
+    auto mma = [&](const u32x4 *Xs, const u32x4 *Ws) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 a[4], b[4];
+            bf16x8 a[4], b[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                a[i] = __builtin_bit_cast(bf16x8, Ws[buf][chunk_at(wn * 64 + 16 * i + li, 4 * kb + kg)]);
+                a[i] = __builtin_bit_cast(bf16x8, Ws[chunk_at(wn * 64 + 16 * i + li, 4 * kb + kg)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b[j] = __builtin_bit_cast(bf16x8, Xs[buf][chunk_at(wm * 64 + 16 * j + li, 4 * kb + kg)]);
+            for (int j = 0; j < 8; ++j)
+                b[j] = __builtin_bit_cast(bf16x8, Xs[chunk_at(wm * 128 + 16 * j + li, 4 * kb + kg)]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < 8; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+    };
+
+    tile_to_lds(x, T, K, m0, 0, X0, wave, lane);
+    tile_to_lds(w, N, K, n0, 0, W0, wave, lane);
+    __syncthreads();
+    const int nk = K / BK;
+    for (int kt = 0; kt < nk; kt += 2) {
+        // K step kt from buffers 0 while step kt + 1 lands in buffers 1, then the other way
         if (kt + 1 < nk) {
-            store_tile(Xs[buf ^ 1], tid, xv);
-            store_tile(Ws[buf ^ 1], tid, wv);
+            tile_to_lds(x, T, K, m0, (kt + 1) * BK, X1, wave, lane);
+            tile_to_lds(w, N, K, n0, (kt + 1) * BK, W1, wave, lane);
         }
+        mma(X0, W0);
         __syncthreads();
+        if (kt + 1 < nk) {
+            if (kt + 2 < nk) {
+                tile_to_lds(x, T, K, m0, (kt + 2) * BK, X0, wave, lane);
+                tile_to_lds(w, N, K, n0, (kt + 2) * BK, W0, wave, lane);
+            }
+            mma(X1, W1);
+            __syncthreads();
+        }
     }
     // lane holds D[4 kg + e][li] of each tile: output columns n .. n+3 of row m
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t m = m0 + wm * 64 + 16 * j + li;
+    for (int j = 0; j < 8; ++j) {
+        const int64_t m = m0 + wm * 128 + 16 * j + li;
         if (m >= T) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -149,10 +158,10 @@ int launch_linear(int64_t T, int K, int N, const void *x, const void *w, void *y
     const dim3 grid((unsigned)((T + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
     hipStream_t st = (hipStream_t)stream;
     if (out_dtype == GDN_BF16)
-        hipLaunchKernelGGL(linear_kernel<uint16_t>, grid, dim3(256), 0, st, (const uint16_t *)x,
+        hipLaunchKernelGGL(linear_kernel<uint16_t>, grid, dim3(kThreads), 0, st, (const uint16_t *)x,
                            (const uint16_t *)w, (uint16_t *)y, T, K, N);
     else
-        hipLaunchKernelGGL(linear_kernel<float>, grid, dim3(256), 0, st, (const uint16_t *)x,
+        hipLaunchKernelGGL(linear_kernel<float>, grid, dim3(kThreads), 0, st, (const uint16_t *)x,
                            (const uint16_t *)w, (float *)y, T, K, N);
     return (int)hipGetLastError();
 }
