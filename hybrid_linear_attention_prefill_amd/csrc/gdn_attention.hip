@@ -190,7 +190,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     f32x4 acc[D / 16];
 #pragma unroll
     for (int i = 0; i < D / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -__builtin_inff(), l = 0.f;
+    // the row sum of the (rounded) weights rides along as one more output tile against a
+    // column of ones: the MFMA sums the 32 keys of a step, every lane gets its row's sum
+    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 ones;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = (__bf16)1.0f;
+    float m = -__builtin_inff();
+    const int64_t p_wave = pos0 + tw;  // the wave's first (smallest) row position
 
     // prologue: blocks 0 and 1 into slots 0 and 1
     Cursor ld = {0, 0, 0};
@@ -252,21 +259,30 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
 
         // softmax update for split j (scores in units of log2: s * c2).  Key 16 kt + sigma(4 g
         // + i) of the split is live for this row when it is at most lim: not past the row's
-        // own position, and inside a staged block.
+        // own position, and inside a staged block.  When every key of the split is live for
+        // every row of the wave, nothing is masked.
         const int64_t key_base = (int64_t)kSplit * j;
         const int64_t rel = prow - key_base;
         const int lim = rel < kBlk * nk - 1 ? (int)rel : kBlk * nk - 1;
-        int sg[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sg[i] = sigma(4 * g + i);
+        const bool full = nk == kSplit / kBlk && p_wave - key_base >= kSplit - 1;
         float mx = -__builtin_inff();
+        if (full) {
 #pragma unroll
-        for (int kt = 0; kt < kSplit / 16; ++kt) {
-            const int lk = lim - 16 * kt;
+            for (int kt = 0; kt < kSplit / 16; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (sg[i] > lk) S[kt][i] = -__builtin_inff();
-                mx = fmaxf(mx, S[kt][i]);
+                for (int i = 0; i < 4; ++i) mx = fmaxf(mx, S[kt][i]);
+        } else {
+            int sg[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sg[i] = sigma(4 * g + i);
+#pragma unroll
+            for (int kt = 0; kt < kSplit / 16; ++kt) {
+                const int lk = lim - 16 * kt;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (sg[i] > lk) S[kt][i] = -__builtin_inff();
+                    mx = fmaxf(mx, S[kt][i]);
+                }
             }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
@@ -274,23 +290,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
         const float m_new = fmaxf(m, mx * c2);
         const float alpha = __builtin_amdgcn_exp2f(m - m_new);
         m = m_new;
-        l *= alpha;
+        lsum *= alpha;
 #pragma unroll
         for (int ct = 0; ct < D / 16; ++ct) acc[ct] *= alpha;
 
-        // weights of the 32 keys 32 kb .. in the lane's key order, rounded to bf16; the row sum
-        // takes the rounded values
+        // weights of the 32 keys 32 kb .. in the lane's key order, rounded to bf16 (a masked
+        // key's -inf gives exactly 0)
         auto weights = [&](int kb) {
             bf16x8 pk;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float sv = S[2 * kb + e / 4][e % 4];
-                const float p = sv == -__builtin_inff()
-                                    ? 0.f
-                                    : __builtin_amdgcn_exp2f(fmaf(sv, c2, -m_new));
-                pk[e] = (__bf16)p;
-                l += (float)pk[e];
-            }
+            for (int e = 0; e < 8; ++e)
+                pk[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * kb + e / 4][e % 4], c2, -m_new));
             return pk;
         };
 #pragma unroll
@@ -300,6 +310,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
 #pragma unroll
                     for (int kb2 = 0; kb2 < 2; ++kb2) {
                         const bf16x8 pk = weights(2 * vc + kb2);
+                        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk, lsum, 0, 0, 0);
                         // V^T fragments of columns ct + 1 .. ct + 2 in flight while ct multiplies
                         bf16x8 vf[4];
                         vf[0] = v_frag<D>(slot, vbase, 0, kb2);
@@ -316,11 +327,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
         }
     }
 
-    // the row's sum from the four lanes that hold it (the same bits in all four)
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
     if (trow < T) {
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / lsum[0];
         Out *orow = (Out *)sq.o + (trow * Hq + h) * D;
 #pragma unroll
         for (int ct = 0; ct < D / 16; ++ct) store4<Out>(orow + 16 * ct + 4 * g, acc[ct] * inv);
