@@ -414,17 +414,32 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__r
 
         // Tinv = (I + A)^-1 by 16 x 16 blocks.  Diagonal blocks by forward substitution
         // (wave hh, lane = 16 b + column).
+        // The strictly lower rows of the block are read as 16-byte pieces, four rows at a
+        // time and all before their use, so that the reads overlap one another instead of each
+        // waiting for the last; a row's sum is accumulated in order over its columns.
         if (wave < nh) {
-            const float *Ah = AS_OF(wave);
+            const float *Ab = AS_OF(wave) + BLK(lane / 16, lane / 16);
             float *Th = TS_OF(wave);
             const int b = lane / 16, jj = lane % 16;
             float xv[16];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = (r == jj) ? 1.f : 0.f;
+            for (int part = 0; part < 4; ++part) {
+                f32x4 ar[4][4];
 #pragma unroll
-                for (int i = 0; i < r; ++i) acc -= Ah[BLK(b, b) + r * BROW + i] * xv[i];
-                xv[r] = acc;
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 4 * part + rr;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (4 * q < r) ar[rr][q] = *(const f32x4 *)(Ab + r * BROW + 4 * q);
+                }
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int r = 4 * part + rr;
+                    float acc = (r == jj) ? 1.f : 0.f;
+#pragma unroll
+                    for (int i = 0; i < r; ++i) acc -= ar[rr][i / 4][i % 4] * xv[i];
+                    xv[r] = acc;
+                }
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) Th[BLK(b, b) + r * BROW + jj] = xv[r];
