@@ -108,6 +108,194 @@ def cpu_baseline(seconds_target=10.0):
                       "16/32/128 layer: %d whole 8192-row calls, %.1f s wall" % (calls, spent)}
 
 
+def session_workloads(b, synth, desc, dev, shape):
+    """Timed session-shaped workloads on the 16/32/128 layer (device time, inputs gathered
+    on the device beforehand and outside the timed regions): a multi-turn replay with forks,
+    a 24-layer long session with checkpoints, a divergence and re-prefill, and 32 batched
+    branches against one prefill per branch."""
+    import numpy as np
+    import torch
+    Hv, d = desc.n_v_heads, desc.d_v
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+
+    def timed(fn, reps=2):
+        fn()  # warm-up
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(reps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps * 1e-3  # seconds per run
+
+    def dev_rows(tab, ids):
+        i = torch.as_tensor(np.asarray(ids, dtype=np.int64), device=dev)
+        return {"x": tab["E"][i], "g": tab["g"][i], "beta": tab["beta"][i]}
+
+    def dev_table(vocab, seed):
+        t = synth.TokenTables(shape, vocab, seed)
+        return {"E": t.E.to(dev), "g": t.g.to(dev), "beta": t.beta.to(dev), "conv_w": t.conv_w.to(dev)}
+
+    res = {}
+    # 1. multi-turn replay: 41,802 tokens in 12 turns; after each turn the whole 512-row chunks
+    #    are committed and the pending tail plus a 40-token question is forked
+    total, n_turns, n_q, vocab, seed = 41802, 12, 40, 4096, 50
+    tab = dev_table(vocab, seed)
+    ids = synth.token_ids(seed, total, vocab)
+    cuts = synth.turn_cuts(seed, total, n_turns)
+    plan, committed = [], 0
+    for t, end in enumerate(cuts):
+        n = ((end - committed) // 512) * 512 if committed % 512 == 0 else 0
+        fork_ids = np.concatenate([ids[committed + n:end], synth.question_ids(seed, t, n_q, vocab)])
+        plan.append((dev_rows(tab, ids[committed:end]), end - committed, dev_rows(tab, fork_ids)))
+        committed += n
+    ws = b.workspace(desc, total)
+    live, fork = b.State(desc), b.State(desc)
+    o = torch.empty((total + n_q, Hv, d), dtype=torch.bfloat16, device=dev)
+
+    def replay():
+        b.gdn_state_init(desc, live)
+        for rows, n, fk in plan:
+            b.gdn_prefill_chunked(desc, rows["x"], tab["conv_w"], rows["g"], rows["beta"], live, live,
+                                  o, n, b.GDN_COMMIT, ws)
+            m = fk["x"].shape[0]
+            b.gdn_prefill_chunked(desc, fk["x"], tab["conv_w"], fk["g"], fk["beta"], live, fork, o, m,
+                                  b.GDN_FORK, ws)
+    sec = timed(replay)
+    fork_rows = sum(fk["x"].shape[0] for _, _, fk in plan)
+    res["multi_turn_replay_41802"] = {
+        "turns": n_turns, "committed_rows": committed, "fork_rows": int(fork_rows),
+        "ms": round(sec * 1e3, 3), "session_tokens_per_s": round(total / sec, 1),
+        "executed_rows_per_s": round((committed + fork_rows) / sec, 1)}
+    del plan, tab, o
+
+    # 2. long session: 24 layers, 100,000 tokens in 6 turns, a checkpoint of every layer at
+    #    each turn end; then a divergence, a restore of the newest checkpoint at or below it
+    #    and a re-prefill of the rest
+    n_layers, total, n_turns, vocab, seed = 24, 100_000, 6, 1024, 60
+    tabs = [dev_table(vocab, 1000 + l) for l in range(n_layers)]
+    ids = synth.token_ids(seed, total, vocab)
+    cuts = synth.turn_cuts(seed, total, n_turns)
+    turns, committed = [], 0
+    for end in cuts:
+        n = ((end - committed) // 512) * 512
+        turns.append((committed, n))
+        committed += n
+    inputs = [dev_rows(tabs[l], ids[:committed]) for l in range(n_layers)]
+    d_pt = synth.divergence_point(seed, 1, total)
+    ckpt_pos = [c + n for c, n in turns]
+    k = max(i for i, p in enumerate([0] + ckpt_pos) if p <= d_pt) - 1
+    p0 = ckpt_pos[k] if k >= 0 else 0
+    ids2 = ids.copy()
+    ids2[d_pt:] = synth.token_ids(seed + 1, total - d_pt, vocab)
+    re_rows = ((total - p0) // 512) * 512
+    inputs2 = [dev_rows(tabs[l], ids2[p0:p0 + re_rows]) for l in range(n_layers)]
+    ws = b.workspace(desc, total)
+    o = torch.empty((total, Hv, d), dtype=torch.bfloat16, device=dev)
+    live = [b.State(desc) for _ in range(n_layers)]
+    slots = [[b.State(desc) for _ in range(n_turns)] for _ in range(n_layers)]
+
+    def session():
+        for l in range(n_layers):
+            b.gdn_state_init(desc, live[l])
+        for t, (c0, n) in enumerate(turns):
+            for l in range(n_layers):
+                x = inputs[l]
+                b.gdn_prefill_chunked(desc, x["x"][c0:c0 + n], tabs[l]["conv_w"], x["g"][c0:c0 + n],
+                                      x["beta"][c0:c0 + n], live[l], live[l], o, n, b.GDN_COMMIT, ws)
+                b.gdn_state_capture(desc, live[l], slots[l][t])
+
+    def divergence():
+        for l in range(n_layers):
+            if k >= 0:
+                b.gdn_state_restore(desc, live[l], slots[l][k])
+            else:
+                b.gdn_state_init(desc, live[l])
+            x = inputs2[l]
+            b.gdn_prefill_chunked(desc, x["x"], tabs[l]["conv_w"], x["g"], x["beta"], live[l], live[l],
+                                  o, re_rows, b.GDN_COMMIT, ws)
+    sec = timed(session, reps=1)
+    sec2 = timed(lambda: (session(), divergence()), reps=1) - sec
+    res["long_session_24_layers_100000"] = {
+        "layers": n_layers, "committed_rows": committed, "turns": n_turns,
+        "ms": round(sec * 1e3, 2), "tokens_per_s_per_layer": round(n_layers * committed / sec, 1),
+        "divergence_at": int(d_pt), "restored_pos": int(p0), "reprefill_rows": int(re_rows),
+        "restore_and_reprefill_ms": round(sec2 * 1e3, 2)}
+    del inputs, inputs2, tabs, o, live, slots
+
+    # 3. prefix sharing: request prefix 1,000, groups with 0/1/70/128 rows of their own, 8
+    #    branches of 1-200 rows per group; prefixes run once up to their last multiple of 64,
+    #    the branches in one batched call from the three shared states; against one plain
+    #    prefill per branch of its whole prompt
+    P, groups, per_group = 1000, [0, 1, 70, 128], 8
+    lens = synth.branch_lengths(31 + P, len(groups) * per_group)
+    tot = P + sum(groups) + sum(lens)
+    dinp = {kk: v.to(dev) for kk, v in synth.layer_inputs(shape, tot, seed=31 + P).items()}
+
+    def sub(idx):
+        i = torch.as_tensor(np.asarray(idx, dtype=np.int64), device=dev)
+        return {kk: v[i] for kk, v in dinp.items() if kk != "conv_w"}
+    gofs, bofs, cur, j = [], [], P, 0
+    for gl in groups:
+        gofs.append((cur, cur + gl))
+        cur += gl
+    for gi in range(len(groups)):
+        for _ in range(per_group):
+            bofs.append((gi, cur, cur + lens[j]))
+            cur += lens[j]
+            j += 1
+    run_req = b.gdn_shared_prefix_rows(0, P)
+    req_in = sub(range(run_req))
+    g_plan = []
+    for (g0, g1) in gofs:
+        idx = list(range(run_req, P)) + list(range(g0, g1))
+        run = b.gdn_shared_prefix_rows(run_req, run_req + len(idx))
+        g_plan.append((sub(idx[:run]) if run else None, run, idx[run:]))
+    rows, cu = [], [0]
+    for (gi, b0, b1) in bofs:
+        idx = g_plan[gi][2] + list(range(b0, b1))
+        rows += idx
+        cu.append(cu[-1] + len(idx))
+    bx = sub(rows)
+    fulls = [sub(list(range(0, P)) + list(range(*gofs[gi])) + list(range(b0, b1)))
+             for (gi, b0, b1) in bofs]
+    ws = b.workspace(desc, tot, 64)
+    o = torch.empty((max(cu[-1], max(f["x"].shape[0] for f in fulls)), Hv, d), dtype=torch.bfloat16,
+                    device=dev)
+    zero, req, gst = b.State(desc), b.State(desc), [b.State(desc) for _ in groups]
+    outs = [b.State(desc) for _ in bofs]
+    b.gdn_state_init(desc, zero)
+    cw = dinp["conv_w"]
+
+    def shared():
+        b.gdn_prefill_chunked(desc, req_in["x"], cw, req_in["g"], req_in["beta"], zero, req, o, run_req,
+                              b.GDN_FORK, ws)
+        inits = []
+        for gi, (gin, run, _) in enumerate(g_plan):
+            if run:
+                b.gdn_prefill_chunked(desc, gin["x"], cw, gin["g"], gin["beta"], req, gst[gi], o, run,
+                                      b.GDN_FORK, ws)
+            inits.append(gst[gi] if run else req)
+        b.gdn_prefill_branches(desc, cu, bx["x"], cw, bx["g"], bx["beta"],
+                               [inits[gi] for (gi, _, _) in bofs], outs, o, ws)
+
+    def per_branch():
+        for k2, f in enumerate(fulls):
+            b.gdn_prefill_chunked(desc, f["x"], cw, f["g"], f["beta"], zero, outs[k2], o, f["x"].shape[0],
+                                  b.GDN_FORK, ws)
+    full_rows = sum(f["x"].shape[0] for f in fulls)
+    executed = run_req + sum(r for _, r, _ in g_plan) + cu[-1]
+    s1, s2 = timed(shared, reps=5), timed(per_branch, reps=5)
+    res["prefix_sharing_32_branches"] = {
+        "request_prefix": P, "executed_rows": int(executed), "full_prompt_rows": int(full_rows),
+        "shared_ms": round(s1 * 1e3, 3), "per_branch_ms": round(s2 * 1e3, 3),
+        "shared_full_prompt_tokens_per_s": round(full_rows / s1, 1),
+        "shared_executed_rows_per_s": round(executed / s1, 1),
+        "per_branch_full_prompt_tokens_per_s": round(full_rows / s2, 1)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,6 +306,9 @@ def main():
                     help="also time state capture/restore, a 370-row fork, decode "
                          "steps of 1 and 32 sessions, the two projections and the full-attention "
                          "layer")
+    ap.add_argument("--workloads", action="store_true",
+                    help="also time the session workloads (multi-turn replay with forks, the "
+                         "24-layer long session, 32 batched branches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run a plain device copy of BYTES bytes three "
                          "times (reference dispatch for the HBM byte counters)")
@@ -290,6 +481,9 @@ def main():
                                        "tflops": round(att_tf, 1),
                                        "mfma_bf16_frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4)}
         del aq, ak, av, ao
+
+    if args.workloads:
+        extras["workloads"] = session_workloads(b, synth, desc, dev, shape)
 
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
