@@ -296,6 +296,48 @@ def session_workloads(b, synth, desc, dev, shape):
     return res
 
 
+def measured_peaks(dev):
+    """Reference rates measured on the box: a 1 GiB device-to-device copy (HBM read + write),
+    and torch's bf16 matmul (the vendor BLAS) at the layer's two projection shapes, beside
+    which the hand-written projection kernel is read."""
+    import torch
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / 10
+    res = {"hbm_copy_GBps": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1),
+           "hbm_copy_frac": round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del src, dst
+    for name, (T, K, N) in (("in_projection", (T_ROWS, 2048, 8256)), ("out_projection", (T_ROWS, 4096, 2048))):
+        x = torch.randn((T, K), device=dev).to(torch.bfloat16)
+        w = (torch.randn((N, K), device=dev) / K ** 0.5).to(torch.bfloat16).t().contiguous()
+        y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(x, w, out=y)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            torch.matmul(x, w, out=y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 20
+        tf = 2.0 * T * K * N / (ms * 1e-3) / 1e12
+        res["torch_matmul_" + name] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                                       "mfma_bf16_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        del x, w, y
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -306,6 +348,9 @@ def main():
                     help="also time state capture/restore, a 370-row fork, decode "
                          "steps of 1 and 32 sessions, the two projections and the full-attention "
                          "layer")
+    ap.add_argument("--peaks", action="store_true",
+                    help="also measure a device copy and torch's bf16 matmul at the projection "
+                         "shapes, as reference rates")
     ap.add_argument("--workloads", action="store_true",
                     help="also time the session workloads (multi-turn replay with forks, the "
                          "24-layer long session, 32 batched branches)")
@@ -484,6 +529,8 @@ def main():
 
     if args.workloads:
         extras["workloads"] = session_workloads(b, synth, desc, dev, shape)
+    if args.peaks:
+        extras["measured_peaks"] = measured_peaks(dev)
 
     if args.copy_calibration:
         # a plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
