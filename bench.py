@@ -335,6 +335,34 @@ def measured_peaks(dev):
         res["torch_matmul_" + name] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
                                        "mfma_bf16_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
         del x, w, y
+    # torch's fused attention, restricted to its flash backend (no fallback to the unfused
+    # path), at the full-attention layer's shape: 16 query heads over 2 key heads of width 256,
+    # causal over 8,192 rows; key heads repeated to the query heads
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        import torch.nn.functional as F
+        Hq, Hkv, D = 16, 2, 256
+        q = torch.randn((1, Hq, T_ROWS, D), device=dev).to(torch.bfloat16)
+        k = torch.randn((1, Hkv, T_ROWS, D), device=dev).to(torch.bfloat16)
+        v = torch.randn((1, Hkv, T_ROWS, D), device=dev).to(torch.bfloat16)
+        k = k.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        v = v.repeat_interleave(Hq // Hkv, dim=1).contiguous()
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for _ in range(2):
+                F.scaled_dot_product_attention(q, k, v, is_causal=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(5):
+                F.scaled_dot_product_attention(q, k, v, is_causal=True)
+            e1.record(stream)
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        tf = 4.0 * D * Hq * (T_ROWS * (T_ROWS + 1) / 2) / (ms * 1e-3) / 1e12
+        res["torch_sdpa_flash_attention"] = {"us": round(ms * 1e3, 2), "tflops": round(tf, 1),
+                                             "mfma_bf16_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        del q, k, v
+    except Exception as e:  # the flash backend may not support this shape or device
+        res["torch_sdpa_flash_attention"] = {"unavailable": str(e)[:200]}
     return res
 
 
