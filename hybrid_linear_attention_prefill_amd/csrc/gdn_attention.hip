@@ -57,19 +57,33 @@ constexpr int kSlotChunks = kBlk * kRowChunks<D>;
 // together with the two chunks per row they also fill 16 distinct slots.
 __device__ __forceinline__ int sigma(int r) { return ((r & 7) << 1) | (r >> 3); }
 
-// One 64-key block (keys key0 .. key0 + 63 of key head kvh) of a [rows][Hkv][D] cache into
-// registers; keys at or past L read as zero.
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// Byte offsets of this thread's chunks of a 64-key block of key head kvh in a [rows][Hkv][D]
+// cache, relative to the block's first key: chunk i is row id / (D / 8), 16-byte column
+// id % (D / 8), with id = tid + 512 i.  Constant for the whole call.
 template <int D>
-__device__ __forceinline__ void blk_load(const uint16_t *base, int64_t key0, int64_t L, int Hkv,
-                                         int kvh, int tid, u32x4 (&v)[D / 64])
+__device__ __forceinline__ void blk_offsets(int Hkv, int kvh, int tid, uint32_t (&off)[D / 64])
 {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
         const int id = tid + kThreads * i, row = id / (D / 8), pc = id % (D / 8);
-        const int64_t key = key0 + row;
-        v[i] = key < L ? *(const u32x4 *)(base + (key * Hkv + kvh) * D + 8 * pc)
-                       : u32x4{0u, 0u, 0u, 0u};
+        off[i] = (uint32_t)(((row * Hkv + kvh) * D + 8 * pc) * 2);
     }
+}
+
+// One 64-key block (keys key0 .. key0 + 63) into registers, through a buffer resource that
+// covers keys key0 .. L - 1 only: its range check reads keys at or past L as zero, so the loads
+// need no compare and no branch.  key0 < L.
+template <int D>
+__device__ __forceinline__ void blk_load(const uint16_t *base, int64_t key0, int64_t L, int Hkv,
+                                         const uint32_t (&off)[D / 64], u32x4 (&v)[D / 64])
+{
+    const int64_t nk = L - key0 < kBlk ? L - key0 : kBlk;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(base + key0 * Hkv * D), 0, (int)(nk * Hkv * D * 2), kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off[i], 0, 0);
 }
 
 template <int D>
@@ -174,6 +188,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     const int64_t trow = tw + li, prow = pos0 + trow;
 
     const uint16_t *kp = (const uint16_t *)sq.k, *vp = (const uint16_t *)sq.v;
+    uint32_t boff[D / 64];
+    blk_offsets<D>(Hkv, kvh, tid, boff);
     const int kbase = sigma(li) * kRowChunks<D> + g;
     const int j4 = lane & 15;
     const int vbase = 16 * sigma(4 * g + j4 / 4) * kRowChunks<D> + 8 * (j4 % 4);
@@ -205,8 +221,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         if (ld.j < ns) {
-            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, kvh, tid,
-                        stage);
+            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, boff, stage);
             blk_store<D>(ring[b], tid, stage);
             advance(ld, ns, nk_last);
         }
@@ -218,8 +233,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     auto step = [&](auto &&work) {
         const bool more = ld.j < ns;
         if (more)
-            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, kvh, tid,
-                        stage);
+            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, boff, stage);
         work(ring[rs]);
         if (more) {
             blk_store<D>(ring[rs == 0 ? 2 : rs - 1], tid, stage);
@@ -251,7 +265,8 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
 #pragma unroll
                         for (int q4 = 0; q4 < 4; ++q4)
                             S[4 * kc + q4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                kf[ks & 1][q4], qf[ks], S[4 * kc + q4], 0, 0, 0);
+                                kf[ks & 1][q4], qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[4 * kc + q4],
+                                0, 0, 0);
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 });
