@@ -813,7 +813,7 @@ int32_t gdn_ckpt_drop_above(gdn_ckpt_ring *r, int64_t d)
     if (!r || r->cap <= 0 || r->cap > GDN_MAX_CHECKPOINTS) return 0;
     int32_t n = 0;
     for (int32_t i = 0; i < r->cap; ++i)
-        if (r->pos[i] > d) {
+        if (r->pos[i] >= 0 && r->pos[i] > d) {  // live slots only (empty ones hold -1)
             r->pos[i] = -1;
             r->age[i] = 0;
             r->n--;
