@@ -285,7 +285,7 @@ gdn_status gdn_desc_check(const gdn_desc *d)
     if (d->act_dtype != GDN_BF16 && d->act_dtype != GDN_F32) return GDN_EINVAL;
     if (d->out_dtype != GDN_BF16 && d->out_dtype != GDN_F32) return GDN_EINVAL;
     if (d->conv_silu != 0 && d->conv_silu != 1) return GDN_EINVAL;
-    if (!(d->l2_eps >= 0.f) || !(d->scale == d->scale)) return GDN_EINVAL;
+    if (!std::isfinite(d->l2_eps) || !(d->l2_eps >= 0.f) || !std::isfinite(d->scale)) return GDN_EINVAL;
     if (d->n_v_heads % d->n_k_heads != 0) return GDN_ESHAPE;
     if (d->d_k != d->d_v || (d->d_k != 64 && d->d_k != 128)) return GDN_ESHAPE;
     if (d->conv_width != 0 && d->conv_width != 4) return GDN_ESHAPE;

@@ -75,7 +75,8 @@ enum { GDN_COMMIT = 0, GDN_FORK = 1 };
 /* Layer description.  Supported by the kernels: d_k == d_v in {64, 128};
  * n_v_heads % n_k_heads == 0; conv_width in {0, 4}; sub_chunk == 64;
  * grid a positive multiple of 64 (512 by default).  scale is the output scale
- * (d_k^-1/2 usually); l2_eps sits inside the square root of the q/k normalisation. */
+ * (d_k^-1/2 usually; finite); l2_eps (finite, >= 0) sits inside the square root of the q/k
+ * normalisation. */
 typedef struct {
     int32_t n_k_heads, n_v_heads, d_k, d_v;
     int32_t conv_width; /* 4, or 0 = inputs already post-conv */

@@ -157,3 +157,37 @@ def test_workspace_grows_with_rows_and_segments(rows, more, segs, d, ratio):
     assert w > 0
     assert b.gdn_workspace_bytes(desc, rows + more, segs) >= w
     assert b.gdn_workspace_bytes(desc, rows, segs + 1) >= w
+
+
+def _desc_ok(f):
+    """The descriptor rules the library documents."""
+    import math
+    nk, nv, dk, dv, cw, sc, grid, act, out, silu, scale, eps = f
+    if min(nk, nv, dk, dv) <= 0 or act not in (0, 1) or out not in (0, 1) or silu not in (0, 1):
+        return False
+    if not (math.isfinite(eps) and eps >= 0 and math.isfinite(scale)):
+        return False
+    if nv % nk or dk != dv or dk not in (64, 128) or cw not in (0, 4) or sc != 64:
+        return False
+    if grid <= 0 or grid % 64:
+        return False
+    return 2 * nk * dk + nv * dv <= 1 << 24
+
+
+small = st.one_of(st.integers(-3, 300), st.sampled_from([-(1 << 31), (1 << 31) - 1, 1 << 20]))
+f32 = st.floats(width=32, allow_nan=True, allow_infinity=True)
+
+
+@SETTINGS
+@given(nk=small, nv=small, dk=st.sampled_from([-1, 0, 32, 64, 100, 128, 256]),
+       dv=st.sampled_from([0, 64, 128, 256]), cw=st.integers(-1, 5), sc=st.sampled_from([0, 32, 64, 128]),
+       grid=st.sampled_from([-512, 0, 1, 64, 100, 512, 2048, 1 << 20]), act=st.integers(-1, 2),
+       out=st.integers(-1, 2), silu=st.integers(-1, 2), scale=f32, eps=f32)
+def test_descriptor_check_matches_its_rules(nk, nv, dk, dv, cw, sc, grid, act, out, silu, scale, eps):
+    f = (nk, nv, dk, dv, cw, sc, grid, act, out, silu, scale, eps)
+    d = b.gdn_desc(*f)
+    ok = b.gdn_desc_check(d) == b.GDN_OK
+    assert ok == _desc_ok(f)
+    # the size queries answer only for valid descriptors
+    assert (b.gdn_state_S_bytes(d) > 0) == ok
+    assert (b.gdn_workspace_bytes(d, 1024, 1) > 0) == ok
