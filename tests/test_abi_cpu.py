@@ -4,6 +4,7 @@ No compute call runs here: every call below is refused by host validation before
 call, or is host-only integer logic.  Fake device addresses are never dereferenced.
 """
 import ctypes
+import os
 import itertools
 
 import pytest
@@ -311,3 +312,33 @@ def test_attention_validation():
     # nothing to do: empty sequences are fine with any pointers
     assert call(seqs=[S(None, None, None, None, 5, 0)]) == b.GDN_OK
     assert call(seqs=[], B=0) == b.GDN_OK
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark runs on one GPU: asked for more it exits with a message, before touching a
+    device (the layer's heads would shard with no exchange step, but that path is not built)."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_bench_algorithmic_counts():
+    """The bench's algorithmic byte and flop counts at the 16/32/128 layer, T = 8192: 24,832
+    bytes per token (bf16 x in, fp32 g and beta, bf16 o) plus the state and window in and out
+    and the conv weights per call; 3.98 MFLOP per token."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bm = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bm)
+    per_token, per_call = bm.algorithmic_bytes(8192, 16, 32, 128)
+    assert per_token == 24832
+    assert per_call == 8192 * 24832 + 2 * 32 * 128 * 128 * 4 + 2 * 3 * 8192 * 2 + 8192 * 4 * 2
+    flops = bm.algorithmic_flops(8192, 16, 32, 128)
+    assert abs(flops / 8192 / 3.98e6 - 1) < 0.01
+    split = bm.kernel_bytes(8192, 16, 32, 128)
+    assert split["prep_kernel"] + split["chain_kernel"] == per_call  # every byte in one kernel
