@@ -85,6 +85,43 @@ static bool states_overlap(const gdn_desc &d, const gdn_state *a, const gdn_stat
             if (overlap(ra.p[i], ra.n[i], rb.p[j], rb.n[j])) return true;
     return false;
 }
+
+// The buffers a prefill reads (x, g, beta, conv weights, the entry states) and writes (o, the
+// workspace bytes it uses, the final states): a written buffer that overlaps any other would
+// race with the kernels that read or write it, so such calls are refused (GDN_EALIAS).
+// `n` rows of x, g, beta and o; entry and final states may be the same state (a commit in
+// place), which the callers check apart.
+static bool io_overlap(const gdn_desc &d, int64_t n, const void *x, const void *conv_w,
+                       const float *g, const float *beta, const void *o, const void *ws,
+                       size_t ws_used, const gdn_state *const *ins, int n_in,
+                       const gdn_state *const *outs, int n_out)
+{
+    const int64_t C = n_channels(d);
+    const size_t xb = (size_t)(n * C) * act_size(d), gb = (size_t)n * d.n_v_heads * 4;
+    const size_t wb = d.conv_width > 0 ? (size_t)C * d.conv_width * act_size(d) : 0;
+    const size_t ob = (size_t)n * d.n_v_heads * d.d_v * out_size(d);
+    const void *rp[4] = {x, g, beta, conv_w};
+    const size_t rn[4] = {xb, gb, gb, wb};
+    const void *wp[2] = {o, ws};
+    const size_t wn[2] = {ob, ws_used};
+    for (int a = 0; a < 2; ++a) {
+        for (int r = 0; r < 4; ++r)
+            if (overlap(wp[a], wn[a], rp[r], rn[r])) return true;
+        if (a == 0 && overlap(wp[0], wn[0], wp[1], wn[1])) return true;
+        for (int k = 0; k < n_in + n_out; ++k) {
+            const Ranges q = ranges_of(d, k < n_in ? ins[k] : outs[k - n_in]);
+            for (int t = 0; t < 2; ++t)
+                if (overlap(wp[a], wn[a], q.p[t], q.n[t])) return true;
+        }
+    }
+    for (int k = 0; k < n_out; ++k) {
+        const Ranges q = ranges_of(d, outs[k]);
+        for (int t = 0; t < 2; ++t)
+            for (int r = 0; r < 4; ++r)
+                if (overlap(q.p[t], q.n[t], rp[r], rn[r])) return true;
+    }
+    return false;
+}
 static bool states_same(const gdn_state *a, const gdn_state *b)
 {
     return a == b || (a->S == b->S && a->conv == b->conv);
@@ -441,9 +478,12 @@ gdn_status gdn_prefill_chunked_events(const gdn_desc *d, const void *x, const vo
             (d->conv_width > 0 && !aligned(conv_w, 16)))
             return GDN_EINVAL;
         const int64_t piece = max_rows_per_launch(*d);
-        if (!ws || ws_bytes < workspace_bytes(*d, (std::min(n, piece) + kC - 1) / kC))
-            return GDN_EWORKSPACE;
+        const size_t ws_used = workspace_bytes(*d, (std::min(n, piece) + kC - 1) / kC);
+        if (!ws || ws_bytes < ws_used) return GDN_EWORKSPACE;
         if (!aligned(ws, 16)) return GDN_EINVAL;
+        const gdn_state *io_in[1] = {in}, *io_out[1] = {out};
+        if (io_overlap(*d, n, x, conv_w, g, beta, o, ws, ws_used, io_in, 1, io_out, 1))
+            return GDN_EALIAS;
         const int64_t pos0 = in->pos;
         const uint64_t tag = in->tag;
         for (int64_t r0 = 0; r0 < n; r0 += piece) {
@@ -522,6 +562,9 @@ gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_
     if (!out) need += (size_t)std::min<int32_t>(B, kMaxSegPerLaunch) * (align256(s_bytes) + c_bytes);
     if (!ws || ws_bytes < need) return GDN_EWORKSPACE;
     if (!aligned(ws, 16)) return GDN_EINVAL;
+    if (io_overlap(*d, cu_rows[B], x, conv_w, g, beta, o, ws, need, init, B,
+                   out ? (const gdn_state *const *)out : nullptr, out ? B : 0))
+        return GDN_EALIAS;
     if (!out) {
         // scratch final states, reused by every launch group (ordered on the stream)
         char *tail = (char *)ws + workspace_bytes(*d, subs);

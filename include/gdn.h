@@ -61,7 +61,7 @@ enum {
     GDN_EMISMATCH = -4,  /* a state's tag is not the descriptor's tag */
     GDN_EWORKSPACE = -5, /* workspace missing or smaller than gdn_workspace_bytes() */
     GDN_EDEVICE = -6,    /* a HIP launch or copy failed */
-    GDN_EALIAS = -7,     /* an output state overlaps memory it must not */
+    GDN_EALIAS = -7,     /* an output (state, o or workspace) overlaps memory it must not */
     GDN_EFILE = -8,      /* a state file is missing, unreadable, truncated or corrupt, or
                             cannot be written */
 };
@@ -198,7 +198,9 @@ gdn_status conv1d_state_step(const gdn_desc *desc, const void *x, const void *co
  * In both modes the arithmetic boundaries are the absolute multiples of 64 only, so a
  * replay split into several calls gives the same bits as one call.
  * x [T][C], g/beta [T][Hv], o [T][Hv][d_v] device; rows_done may be NULL.  ws must hold
- * gdn_workspace_bytes(desc, T, 1) bytes (device).  Both states' tags must match. */
+ * gdn_workspace_bytes(desc, T, 1) bytes (device).  Both states' tags must match.  o, the
+ * workspace bytes used and the out state may overlap none of the other buffers of the call
+ * (GDN_EALIAS), apart from out being in itself in a commit. */
 gdn_status gdn_prefill_chunked(const gdn_desc *desc, const void *x, const void *conv_w,
                                const float *g, const float *beta, const gdn_state *in,
                                gdn_state *out, void *o, int64_t T, int32_t mode,
@@ -221,8 +223,9 @@ gdn_status gdn_prefill_chunked_events(const gdn_desc *desc, const void *x, const
  * non-decreasing offsets starting at 0; every branch has >= 1 row) and starts from
  * init[b], whose pos must be a multiple of 64.  init entries may repeat (a shared prefix
  * state, read only).  out may be NULL (no final states), else out[b] receives branch b's
- * final state; no out[b] may overlap any init state or another out.  ws must hold
- * gdn_workspace_bytes(desc, cu_rows[B], B) bytes.  Each branch's rows and final state
+ * final state; no out[b] may overlap any init state or another out, and o, the workspace
+ * bytes used and the out states may overlap none of x, g, beta, conv_w or each other
+ * (GDN_EALIAS).  ws must hold gdn_workspace_bytes(desc, cu_rows[B], B) bytes.  Each branch's rows and final state
  * are bitwise those of a single-sequence gdn_prefill_chunked(GDN_FORK) from init[b]. */
 gdn_status gdn_prefill_branches(const gdn_desc *desc, int32_t B, const int64_t *cu_rows,
                                 const void *x, const void *conv_w, const float *g,

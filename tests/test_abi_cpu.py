@@ -77,8 +77,12 @@ def _state(pos=0, tag=None, S=FAKE, conv=FAKE + (1 << 30)):
     return s
 
 
+# distinct fake device addresses for the buffers of a call (states sit at FAKE and FAKE + 1 GiB)
+X_, W_, G_, B_, O_ = (FAKE + (k << 30) for k in (10, 11, 12, 13, 14))
+
+
 def _chunked(d, sin, sout, T=512, mode=b.GDN_COMMIT, ws=FAKE + (2 << 30), ws_bytes=1 << 40,
-             x=FAKE, conv_w=FAKE, g=FAKE, beta=FAKE, o=FAKE):
+             x=X_, conv_w=W_, g=G_, beta=B_, o=O_):
     rows = ctypes.c_int64(-7)
     st = b.lib.gdn_prefill_chunked(ctypes.byref(d), x, conv_w, g, beta, ctypes.byref(sin),
                                    ctypes.byref(sout), o, T, mode, ctypes.byref(rows), ws,
@@ -105,11 +109,18 @@ def test_prefill_validation_refuses_before_device_work():
         # overlapping but not identical output state in a commit
         (dict(sin=s, sout=_state(pos=512, S=FAKE + 64, conv=FAKE + (7 << 30))), b.GDN_EALIAS),
         # misaligned device pointers
-        (dict(sin=s, sout=s, x=FAKE + 2), b.GDN_EINVAL),
-        (dict(sin=s, sout=s, o=FAKE + 8), b.GDN_EINVAL),
-        (dict(sin=s, sout=s, conv_w=FAKE + 4), b.GDN_EINVAL),
-        (dict(sin=s, sout=s, g=FAKE + 2), b.GDN_EINVAL),
-        (dict(sin=s, sout=s, beta=FAKE + 1), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, x=X_ + 2), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, o=O_ + 8), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, conv_w=W_ + 4), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, g=G_ + 2), b.GDN_EINVAL),
+        (dict(sin=s, sout=s, beta=B_ + 1), b.GDN_EINVAL),
+        # written buffers overlapping anything else the call touches
+        (dict(sin=s, sout=s, o=X_ + (1 << 20)), b.GDN_EALIAS),                     # o inside x
+        (dict(sin=s, sout=s, o=G_), b.GDN_EALIAS),                                 # o on g
+        (dict(sin=s, sout=s, ws=O_ + 4096), b.GDN_EALIAS),                         # workspace in o
+        (dict(sin=s, sout=s, ws=W_), b.GDN_EALIAS),                                # workspace on conv w
+        (dict(sin=s, sout=s, o=FAKE + 4096), b.GDN_EALIAS),                        # o in the state
+        (dict(sin=s, sout=_state(pos=512, S=X_, conv=FAKE + (7 << 30))), b.GDN_EALIAS),  # S out on x
         (dict(sin=_state(pos=512, S=FAKE + 2), sout=_state(pos=512, S=FAKE + 2)), b.GDN_EINVAL),
         (dict(sin=s, sout=_state(pos=512, S=FAKE + (15 << 30), conv=FAKE + (16 << 30) + 8)),
          b.GDN_EINVAL),
@@ -128,12 +139,12 @@ def test_branches_validation():
     s = _state(pos=960)
     sp = ctypes.pointer(s)
 
-    def call(B, cu, inits, outs=None, ws_bytes=1 << 40):
+    def call(B, cu, inits, outs=None, ws_bytes=1 << 40, x=X_, o=O_):
         cu_a = (ctypes.c_int64 * len(cu))(*cu)
         ia = (ctypes.POINTER(b.gdn_state) * B)(*inits)
         oa = None if outs is None else (ctypes.POINTER(b.gdn_state) * B)(*outs)
-        return b.lib.gdn_prefill_branches(ctypes.byref(d), B, cu_a, FAKE, FAKE, FAKE, FAKE, ia,
-                                          oa, FAKE, FAKE + (3 << 30), ws_bytes, None)
+        return b.lib.gdn_prefill_branches(ctypes.byref(d), B, cu_a, x, W_, G_, B_, ia,
+                                          oa, o, FAKE + (3 << 30), ws_bytes, None)
 
     assert call(2, [0, 10, 10], [sp, sp]) == b.GDN_EINVAL            # empty branch
     assert call(1, [5, 10], [sp]) == b.GDN_EINVAL                     # offsets must start at 0
@@ -147,6 +158,10 @@ def test_branches_validation():
     assert call(1, [0, 10], [sp], ws_bytes=10) == b.GDN_EWORKSPACE
     foreign = _state(pos=0, tag=99)
     assert call(1, [0, 10], [ctypes.pointer(foreign)]) == b.GDN_EMISMATCH
+    assert call(1, [0, 10], [sp], o=X_) == b.GDN_EALIAS                # o on x
+    assert call(1, [0, 10], [sp], o=FAKE + 64) == b.GDN_EALIAS         # o in an entry state
+    o2 = _state(S=X_ + 256, conv=FAKE + (9 << 30))
+    assert call(1, [0, 10], [sp], [ctypes.pointer(o2)]) == b.GDN_EALIAS  # final S on x
 
 
 def test_decode_validation_refuses_before_device_work():
