@@ -616,6 +616,9 @@ gdn_status gdn_decode_step(const gdn_desc *d, int32_t B, const void *x, const vo
             if (j < b && states_overlap(*d, out[b], out[j])) return GDN_EALIAS;
         }
     }
+    // o may overlap no input and no state; no final state may overlap an input
+    if (io_overlap(*d, B, x, conv_w, g, beta, o, nullptr, 0, in, B, (const gdn_state *const *)out, B))
+        return GDN_EALIAS;
     std::vector<int64_t> pos0((size_t)B);
     for (int32_t b = 0; b < B; ++b) pos0[b] = in[b]->pos;
     const uint64_t tag = gdn_desc_tag(d);
@@ -728,6 +731,8 @@ gdn_status gdn_linear(int64_t T, int32_t K, int32_t N, const void *x, const void
     if (T > (int64_t)INT32_MAX * 128) return GDN_EINVAL;
     if (T == 0) return GDN_OK;
     if (!x || !w || !y || !aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return GDN_EINVAL;
+    const size_t yb = (size_t)T * N * (out_dtype == GDN_BF16 ? 2 : 4);
+    if (overlap(y, yb, x, (size_t)T * K * 2) || overlap(y, yb, w, (size_t)N * K * 2)) return GDN_EALIAS;
     if (launch_linear(T, K, N, x, w, y, out_dtype, stream) != 0) return GDN_EDEVICE;
     return GDN_OK;
 }

@@ -247,7 +247,8 @@ gdn_status gdn_prefill_branches(const gdn_desc *desc, int32_t B, const int64_t *
  * 16-byte aligned here (the step moves it in 16-byte pieces).  in[b] is read,
  * out[b] receives the advanced state (pos = in[b]->pos + 1, the tag kept); out[b] may be
  * in[b] itself (in place).  in entries may repeat (a shared read-only state), but no out[b]
- * may overlap an in[j] or out[j] of another sequence (GDN_EALIAS).  There is no position
+ * may overlap an in[j] or out[j] of another sequence, o may overlap no input or state, and
+ * no out[b] may overlap x, g, beta or conv_w (GDN_EALIAS).  There is no position
  * constraint: a decoded state sits off the 64-row grid, so only further decode steps
  * continue it (a prefill refuses it with GDN_EGRID).  The result matches the per-token rule
  * to fp32 rounding; it is not bitwise a GDN_FORK prefill of the same row, whose chunk
@@ -267,7 +268,8 @@ gdn_status gdn_decode_step(const gdn_desc *desc, int32_t B, const void *x, const
  * bits as a run over all of them (PR "qwen3_5: run prompts that share prefixes once per
  * prefix", section Purpose, "GEMMs": one fixed algorithm per weight shape, so grouped runs
  * equal a plain pass bit for bit).  Requires K % 64 == 0, N % 16 == 0, T >= 0 (T == 0 does
- * nothing); x, w, y device pointers, 16-byte aligned.  Asynchronous on `stream`. */
+ * nothing); x, w, y device pointers, 16-byte aligned; y may overlap neither x nor w
+ * (GDN_EALIAS).  Asynchronous on `stream`. */
 gdn_status gdn_linear(int64_t T, int32_t K, int32_t N, const void *x, const void *w, void *y,
                       int32_t out_dtype, void *stream);
 

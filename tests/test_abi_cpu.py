@@ -170,7 +170,7 @@ def test_decode_validation_refuses_before_device_work():
     c = _state(pos=33, S=FAKE + (20 << 30), conv=FAKE + (21 << 30))
     ap, cp = ctypes.pointer(a), ctypes.pointer(c)
 
-    def call(B, inits, outs, x=FAKE, conv_w=FAKE, g=FAKE, beta=FAKE, o=FAKE, desc=d):
+    def call(B, inits, outs, x=X_, conv_w=W_, g=G_, beta=B_, o=O_, desc=d):
         ia = None if inits is None else (ctypes.POINTER(b.gdn_state) * max(B, 1))(*inits)
         oa = None if outs is None else (ctypes.POINTER(b.gdn_state) * max(B, 1))(*outs)
         return b.lib.gdn_decode_step(ctypes.byref(desc), B, x, conv_w, g, beta, ia, oa, o, None)
@@ -179,8 +179,12 @@ def test_decode_validation_refuses_before_device_work():
     assert call(1, None, [ap]) == b.GDN_EINVAL
     assert call(1, [ap], None) == b.GDN_EINVAL
     for kw in (dict(x=None), dict(g=None), dict(beta=None), dict(o=None), dict(conv_w=None),
-               dict(x=FAKE + 2), dict(o=FAKE + 8), dict(g=FAKE + 2), dict(conv_w=FAKE + 4)):
+               dict(x=X_ + 2), dict(o=O_ + 8), dict(g=G_ + 2), dict(conv_w=W_ + 4)):
         assert call(1, [ap], [ap], **kw) == b.GDN_EINVAL, kw
+    # the output row overlapping the input row, a gate, or the state it updates
+    assert call(1, [ap], [ap], o=X_ + 1024) == b.GDN_EALIAS
+    assert call(1, [ap], [ap], o=B_) == b.GDN_EALIAS
+    assert call(1, [ap], [ap], o=FAKE + 512) == b.GDN_EALIAS
     foreign = _state(tag=77)
     assert call(1, [ctypes.pointer(foreign)], [ctypes.pointer(foreign)]) == b.GDN_EMISMATCH
     # a shared input updated in place by one sequence while another reads it
@@ -200,13 +204,16 @@ def test_decode_validation_refuses_before_device_work():
 
 
 def test_linear_validation():
-    def call(T=64, K=128, N=32, x=FAKE, w=FAKE, y=FAKE, od=b.GDN_BF16):
+    def call(T=64, K=128, N=32, x=X_, w=W_, y=O_, od=b.GDN_BF16):
         return b.lib.gdn_linear(T, K, N, x, w, y, od, None)
 
     for kw in (dict(K=96), dict(K=0), dict(N=24), dict(N=0), dict(T=-1), dict(od=5),
-               dict(x=None), dict(w=None), dict(y=None), dict(x=FAKE + 8), dict(y=FAKE + 4)):
+               dict(x=None), dict(w=None), dict(y=None), dict(x=X_ + 8), dict(y=O_ + 4)):
         assert call(**kw) == b.GDN_EINVAL, kw
     assert call(T=0, x=None, w=None, y=None) == b.GDN_OK  # nothing to do, nothing touched
+    # the output overlapping an input: x (64 x 128 bf16 = 16 KiB) or w
+    assert call(y=X_ + 4096) == b.GDN_EALIAS
+    assert call(y=W_ - 1024) == b.GDN_EALIAS
 
 
 def test_state_ops_validation():
