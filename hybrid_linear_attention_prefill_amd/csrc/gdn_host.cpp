@@ -435,6 +435,16 @@ gdn_status conv1d_state_step(const gdn_desc *d, const void *x, const void *conv_
     if (T < 0 || T > INT32_MAX) return GDN_EINVAL;
     if (!conv_w || !window || (T > 0 && (!x || !y))) return GDN_EINVAL;
     if (T == 0) return GDN_OK;
+    {
+        // y and the window are written: neither may overlap x, the weights or each other
+        const int64_t C = n_channels(*d);
+        const size_t xb = (size_t)(T * C) * act_size(*d), yb = (size_t)(T * C) * out_size(*d);
+        const size_t wb = (size_t)C * d->conv_width * act_size(*d);
+        const size_t nb = (size_t)(d->conv_width - 1) * C * act_size(*d);
+        if (overlap(y, yb, x, xb) || overlap(y, yb, conv_w, wb) || overlap(y, yb, window, nb) ||
+            overlap(window, nb, x, xb) || overlap(window, nb, conv_w, wb))
+            return GDN_EALIAS;
+    }
     if (launch_conv_step(*d, x, conv_w, window, y, T, stream) != 0) return GDN_EDEVICE;
     return GDN_OK;
 }

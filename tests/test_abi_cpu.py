@@ -234,6 +234,10 @@ def test_state_ops_validation():
     assert b.lib.conv1d_state_step(ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, -1, None) == b.GDN_EINVAL
     # T == 0 is a no-op that touches nothing
     assert b.lib.conv1d_state_step(ctypes.byref(d), None, FAKE, FAKE, None, 0, None) == b.GDN_OK
+    # written buffers (y, window) overlapping another buffer of the call
+    assert b.lib.conv1d_state_step(ctypes.byref(d), X_, W_, FAKE, X_ + 64, 8, None) == b.GDN_EALIAS
+    assert b.lib.conv1d_state_step(ctypes.byref(d), X_, W_, X_ + 16, O_, 8, None) == b.GDN_EALIAS
+    assert b.lib.conv1d_state_step(ctypes.byref(d), X_, W_, FAKE, FAKE + 8, 8, None) == b.GDN_EALIAS
 
 
 def test_commit_rows_exhaustive():
