@@ -10,11 +10,14 @@
 // row's place in its tile or the grid; there is no split-K and no shape-dependent choice.
 //
 // Tile: 256 rows x 256 output columns per workgroup of 8 waves, each wave owning 128 rows x 64
-// columns (8 x 4 MFMA tiles of 16 x 16).  K advances in steps of 64, double-buffered in LDS; the
-// next step's tiles are copied from global memory straight into LDS (no registers) while the
-// current one is multiplied.  The MFMA computes D = W X^T (16 output columns x 16 rows), so
-// that a lane holds four adjacent output columns of one row and stores them with one 8- or
-// 16-byte store.
+// columns (8 x 4 MFMA tiles of 16 x 16).  Columns past the last multiple of 256 go to a second
+// launch of 256 x 64 tiles (eight waves of 32 rows x 64 columns), so that a remainder such as
+// the 64 gate columns of an 8,256-wide in-projection costs a quarter of a full tile instead of
+// a whole one.  Both widths run the same MFMA over the same K blocks for every element, so
+// they give the same bits.  K advances in steps of 64, double-buffered in LDS; the next step's
+// tiles are copied from global memory straight into LDS (no registers) while the current one
+// is multiplied.  The MFMA computes D = W X^T (16 output columns x 16 rows), so that a lane
+// holds four adjacent output columns of one row and stores them with one 8- or 16-byte store.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -30,7 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 8;  // CH 16-byte chunks per tile row
+constexpr int BM = 256, BK = 64, CH = BK / 8;  // CH 16-byte chunks per tile row
 constexpr int kThreads = 512;
 
 // 16-byte chunk c of row r of an LDS tile (rows of 128 bytes): the chunk index is XORed with
@@ -58,78 +61,83 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v)
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// One 256-row x 64-K tile of a row-major [rows][ld] bf16 matrix, rows from r0, copied from
+// One ROWS-row x 64-K tile of a row-major [rows][ld] bf16 matrix, rows from r0, copied from
 // global memory into the LDS tile L by direct-to-LDS loads.  Each wave instruction fills 1 KB of
-// LDS in lane order, so lane i of instruction j fills position p = 64 (4 wave + j) + i, and
+// LDS in lane order, so lane i of instruction j fills position p = 64 (J wave + j) + i, and
 // fetches the chunk that the swizzle puts there.  Rows at or past `rows` repeat the last row:
 // they only feed outputs that are never stored.
+template <int ROWS>
 __device__ __forceinline__ void tile_to_lds(const uint16_t *M, int64_t rows, int64_t ld, int64_t r0,
                                             int k0, u32x4 *L, int wave, int lane)
 {
+    constexpr int J = ROWS * CH / (64 * 8);  // wave instructions per wave
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int p = 64 * (4 * wave + j) + lane, r = p / CH, c = (p % CH) ^ ((r >> 1) & 7);
+    for (int j = 0; j < J; ++j) {
+        const int p = 64 * (J * wave + j) + lane, r = p / CH, c = (p % CH) ^ ((r >> 1) & 7);
         const int64_t gr = r0 + r < rows ? r0 + r : rows - 1;
         __builtin_amdgcn_global_load_lds((const void *)(M + gr * ld + k0 + 8 * c),
-                                         (lds_void *)(L + 64 * (4 * wave + j)), 16, 0, 0);
+                                         (lds_void *)(L + 64 * (J * wave + j)), 16, 0, 0);
     }
 }
 
-template <typename Out>
+// y[:, 0 .. N) (row stride ldy) of a BM x BN tile grid; BN is 256 or 64.
+template <typename Out, int BN>
 __global__ __launch_bounds__(kThreads) void linear_kernel(const uint16_t *__restrict__ x,
                                                           const uint16_t *__restrict__ w,
                                                           Out *__restrict__ y, int64_t T, int K,
-                                                          int N)
+                                                          int N, int64_t ldy)
 {
+    constexpr int NWN = BN / 64, NWM = 8 / NWN;  // waves along N and along M
+    constexpr int WM = BM / NWM, RT = WM / 16;   // rows per wave, 16-row MFMA tiles per wave
     // two separate buffers (not one array indexed by parity): the compiler then sees that the
     // copies into one do not alias the reads of the other, and does not wait for them early
     __shared__ u32x4 X0[BM * CH], W0[BN * CH], X1[BM * CH], W1[BN * CH];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;  // this wave's 128 x 64 part
+    const int wm = wave % NWM, wn = wave / NWM;  // this wave's WM x 64 part
     const int64_t m0 = (int64_t)blockIdx.x * BM;
     const int64_t n0 = (int64_t)blockIdx.y * BN;
     const int li = lane % 16, kg = lane / 16;
 
-    f32x4 acc[4][8];  // [output column tile i][row tile j]
+    f32x4 acc[4][RT];  // [output column tile i][row tile j]
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < RT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto mma = [&](const u32x4 *Xs, const u32x4 *Ws) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            bf16x8 a[4], b[8];
+            bf16x8 a[4], b[RT];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 a[i] = __builtin_bit_cast(bf16x8, Ws[chunk_at(wn * 64 + 16 * i + li, 4 * kb + kg)]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                b[j] = __builtin_bit_cast(bf16x8, Xs[chunk_at(wm * 128 + 16 * j + li, 4 * kb + kg)]);
+            for (int j = 0; j < RT; ++j)
+                b[j] = __builtin_bit_cast(bf16x8, Xs[chunk_at(wm * WM + 16 * j + li, 4 * kb + kg)]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < RT; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     };
 
-    tile_to_lds(x, T, K, m0, 0, X0, wave, lane);
-    tile_to_lds(w, N, K, n0, 0, W0, wave, lane);
+    tile_to_lds<BM>(x, T, K, m0, 0, X0, wave, lane);
+    tile_to_lds<BN>(w, N, K, n0, 0, W0, wave, lane);
     __syncthreads();
     const int nk = K / BK;
     for (int kt = 0; kt < nk; kt += 2) {
         // K step kt from buffers 0 while step kt + 1 lands in buffers 1, then the other way
         if (kt + 1 < nk) {
-            tile_to_lds(x, T, K, m0, (kt + 1) * BK, X1, wave, lane);
-            tile_to_lds(w, N, K, n0, (kt + 1) * BK, W1, wave, lane);
+            tile_to_lds<BM>(x, T, K, m0, (kt + 1) * BK, X1, wave, lane);
+            tile_to_lds<BN>(w, N, K, n0, (kt + 1) * BK, W1, wave, lane);
         }
         mma(X0, W0);
         __syncthreads();
         if (kt + 1 < nk) {
             if (kt + 2 < nk) {
-                tile_to_lds(x, T, K, m0, (kt + 2) * BK, X0, wave, lane);
-                tile_to_lds(w, N, K, n0, (kt + 2) * BK, W0, wave, lane);
+                tile_to_lds<BM>(x, T, K, m0, (kt + 2) * BK, X0, wave, lane);
+                tile_to_lds<BN>(w, N, K, n0, (kt + 2) * BK, W0, wave, lane);
             }
             mma(X1, W1);
             __syncthreads();
@@ -137,15 +145,30 @@ __global__ __launch_bounds__(kThreads) void linear_kernel(const uint16_t *__rest
     }
     // lane holds D[4 kg + e][li] of each tile: output columns n .. n+3 of row m
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int64_t m = m0 + wm * 128 + 16 * j + li;
+    for (int j = 0; j < RT; ++j) {
+        const int64_t m = m0 + wm * WM + 16 * j + li;
         if (m >= T) continue;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int64_t n = n0 + wn * 64 + 16 * i + 4 * kg;
-            if (n < N) store4<Out>(y + m * N + n, acc[i][j]);
+            if (n < N) store4<Out>(y + m * ldy + n, acc[i][j]);
         }
     }
+}
+
+template <typename Out>
+int launch_tiles(int64_t T, int K, int N, const uint16_t *x, const uint16_t *w, Out *y, hipStream_t st)
+{
+    const unsigned gm = (unsigned)((T + BM - 1) / BM);
+    const int nw = N / 256 * 256;  // columns in whole 256-wide tiles
+    if (nw > 0)
+        hipLaunchKernelGGL((linear_kernel<Out, 256>), dim3(gm, (unsigned)(nw / 256)), dim3(kThreads), 0,
+                           st, x, w, y, T, K, nw, (int64_t)N);
+    if (N > nw)
+        hipLaunchKernelGGL((linear_kernel<Out, 64>), dim3(gm, (unsigned)((N - nw + 63) / 64)),
+                           dim3(kThreads), 0, st, x, w + (int64_t)nw * K, y + nw, T, K, N - nw,
+                           (int64_t)N);
+    return (int)hipGetLastError();
 }
 
 }  // namespace
@@ -155,15 +178,10 @@ int launch_linear(int64_t T, int K, int N, const void *x, const void *w, void *y
 {
     (void)hipGetLastError();
     if (T == 0) return 0;
-    const dim3 grid((unsigned)((T + BM - 1) / BM), (unsigned)((N + BN - 1) / BN));
     hipStream_t st = (hipStream_t)stream;
     if (out_dtype == GDN_BF16)
-        hipLaunchKernelGGL(linear_kernel<uint16_t>, grid, dim3(kThreads), 0, st, (const uint16_t *)x,
-                           (const uint16_t *)w, (uint16_t *)y, T, K, N);
-    else
-        hipLaunchKernelGGL(linear_kernel<float>, grid, dim3(kThreads), 0, st, (const uint16_t *)x,
-                           (const uint16_t *)w, (float *)y, T, K, N);
-    return (int)hipGetLastError();
+        return launch_tiles<uint16_t>(T, K, N, (const uint16_t *)x, (const uint16_t *)w, (uint16_t *)y, st);
+    return launch_tiles<float>(T, K, N, (const uint16_t *)x, (const uint16_t *)w, (float *)y, st);
 }
 
 }  // namespace gdn

@@ -41,7 +41,8 @@ def _run(b, x, w, dtype):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("T,K,N", [(300, 256, 272), (1, 64, 16), (129, 192, 144), (64, 512, 128)])
 def test_linear_matches_oracle(b, T, K, N, dtype):
-    """Ragged row tiles (300 = 2 x 128 + 44), a 16-column tail tile, one row, one K step."""
+    """Ragged row tiles (300 = 256 + 44), a 16-column tail tile after a full 256-column one,
+    one row, column counts below 256 (narrow tiles only), one K step."""
     x, w = synth.linear_inputs(T, K, N, seed=T + K)
     y = _run(b, x.cuda(), w.cuda(), dtype)
     torch.cuda.synchronize()
@@ -53,7 +54,7 @@ def test_linear_matches_oracle(b, T, K, N, dtype):
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_rows_are_invariant_to_the_call(b, dtype):
     """Rows a .. b-1 computed alone equal the same rows of one call over all rows, bit for bit,
-    wherever the range starts and ends relative to the 128-row tiles."""
+    wherever the range starts and ends relative to the 256-row tiles."""
     T, K, N = 300, 256, 272
     x, w = synth.linear_inputs(T, K, N, seed=5)
     xd, wd = x.cuda(), w.cuda()
@@ -61,6 +62,24 @@ def test_rows_are_invariant_to_the_call(b, dtype):
     for a, e in ((0, 1), (37, 300), (128, 256), (255, 257), (1, 129), (299, 300), (0, 300)):
         part = _run(b, xd[a:e], wd, dtype)
         assert same_bits(part, full[a:e]), (a, e)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_columns_are_invariant_to_the_tile_width(b, dtype):
+    """Columns past the last multiple of 256 run in 64-wide tiles, the rest in 256-wide ones.
+    A column gives the same bits in either: w[:320] puts columns 0-63 in a wide tile and
+    256-319 in a narrow one; w[:64] alone runs narrow, w[64:320] alone runs wide."""
+    T, K = 300, 192
+    x, w = synth.linear_inputs(T, K, 320, seed=8)
+    xd, wd = x.cuda(), w.cuda()
+    full = _run(b, xd, wd, dtype)
+    narrow = _run(b, xd, wd[:64].contiguous(), dtype)
+    wide = _run(b, xd, wd[64:].contiguous(), dtype)
+    torch.cuda.synchronize()
+    assert same_bits(narrow, full[:, :64])
+    assert same_bits(wide[:, 192:], full[:, 256:])
+    assert same_bits(wide[:, :192], full[:, 64:256])
+    assert rel_l2(full.float().cpu().numpy(), _oracle(x, w)) < (FP32_TOL if dtype == torch.float32 else TOL)
 
 
 def test_zero_rows_and_output_untouched_outside(b):
