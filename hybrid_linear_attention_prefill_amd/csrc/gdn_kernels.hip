@@ -707,9 +707,10 @@ __device__ __forceinline__ void conv_bv(ChainLds<D, Act> &L, const ChainArgs &a,
     *(f32x4 *)(L.bv + a.col * CL::BS + r0) = bvv;
 }
 
-// One step of a state wave over sub-chunk `cl` with register set K (step index modulo 3).
-template <int K, int D, typename Act>
-__device__ __forceinline__ void state_step(ChainLds<D, Act> &L, StateRegs<D> (&R)[3], const ChainArgs &a,
+// One step of a state wave over sub-chunk `cl` with register set K (step index modulo NB, the
+// depth of the prefetch ring: the loads of a sub-chunk go out NB - 1 steps before its own).
+template <int K, int NB, int D, typename Act>
+__device__ __forceinline__ void state_step(ChainLds<D, Act> &L, StateRegs<D> (&R)[NB], const ChainArgs &a,
                                            int cl, int nsub, f32x4 (&S)[D / 64], const Workspace &ws)
 {
     using CL = ChainLds<D, Act>;
@@ -723,8 +724,8 @@ __device__ __forceinline__ void state_step(ChainLds<D, Act> &L, StateRegs<D> (&R
     // B fragments stay 16 contiguous bytes: row 16w + 4kg + i sits at position pr0 + i.
     const int pr0 = 32 * (wave / 2) + 8 * kg + 4 * (wave % 2);
     const float *F = L.fac[cl & 1];
-    const int cn = min(cl + 2, nsub - 1);  // the sub-chunk whose inputs this step prefetches
-    state_issue<D, 1>(R[(K + 2) % 3], a, cn, ws);
+    const int cn = min(cl + NB - 1, nsub - 1);  // the sub-chunk whose inputs this step prefetches
+    state_issue<D, 1>(R[(K + NB - 1) % NB], a, cn, ws);
 
     // phase 1: X = K S for row tile `wave`; R = beta v - beta gamma X
     f32x4 X = {0.f, 0.f, 0.f, 0.f};
@@ -743,7 +744,7 @@ __device__ __forceinline__ void state_step(ChainLds<D, Act> &L, StateRegs<D> (&R
 
     // phase 2: D = Tinv R (fragments above the diagonal are zero); this step's K rows for the
     // transposed reads of phase 3
-    state_issue<D, 2>(R[(K + 2) % 3], a, cn, ws);
+    state_issue<D, 2>(R[(K + NB - 1) % NB], a, cn, ws);
     f32x4 Dl = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -805,12 +806,13 @@ __device__ __forceinline__ void out_store(const ChainLds<D, Act> &L, const Chain
     store_out4<Out>(a.ro, obase, Oa * scale);
 }
 
-// One step of an output wave over sub-chunk `cl` with register set K.  Ob and mcur carry gamma P
-// and the M fragments of the previous sub-chunk into this step's phase 1.  The raw v rows,
-// which come from HBM, are loaded three steps ahead: set K holds those of sub-chunk cl + 3
-// (its previous rows, of sub-chunk cl, went to LDS one step ago).
-template <int K, int D, typename Act, typename Out, bool SILU>
-__device__ __forceinline__ void out_step(ChainLds<D, Act> &L, OutRegs<D, Act> (&R)[3], const ChainArgs &a,
+// One step of an output wave over sub-chunk `cl` with register set K (of NB).  Ob and mcur carry
+// gamma P and the M fragments of the previous sub-chunk into this step's phase 1.  Q and M are
+// loaded NB - 1 steps ahead; the raw v rows, which come from HBM, NB steps ahead: set K then
+// takes those of sub-chunk cl + NB (its previous rows, of sub-chunk cl, went to LDS one step
+// ago).
+template <int K, int NB, int D, typename Act, typename Out, bool SILU>
+__device__ __forceinline__ void out_step(ChainLds<D, Act> &L, OutRegs<D, Act> (&R)[NB], const ChainArgs &a,
                                          int cl, int nsub, f32x4 &Ob, half8 (&mcur)[2], float w0,
                                          float w1, float w2, float w3, float scale,
                                          const Workspace &ws)
@@ -818,13 +820,13 @@ __device__ __forceinline__ void out_step(ChainLds<D, Act> &L, OutRegs<D, Act> (&
     using OR = OutRegs<D, Act>;
     const OutRegs<D, Act> &C = R[K];
     const int col = a.col, kg = a.kg;
-    const int cn = min(cl + 2, nsub - 1);
+    const int cn = min(cl + NB - 1, nsub - 1);
 
     // phase 1: O of the previous sub-chunk (its D^T is in LDS until this step's phase 2); the
     // next sub-chunk's raw v rows and factors
     if (cl > 0) out_store<D, Act, Out>(L, a, cl - 1, Ob, mcur, scale);
-    put_ld<D, Act>(L, R[(K + 1) % 3], a, (cl + 1) & 1, nullptr);
-    out_issue<D, Act, 3>(R[K], a, min(cl + 3, nsub - 1), ws);
+    put_ld<D, Act>(L, R[(K + 1) % NB], a, (cl + 1) & 1, nullptr);
+    out_issue<D, Act, 3>(R[K], a, min(cl + NB, nsub - 1), ws);
     __syncthreads();  // #1
 
     // phase 2: P = Q S, transposed (D^T of S^T Q^T): this lane's row 16 wave + col, columns
@@ -836,17 +838,19 @@ __device__ __forceinline__ void out_step(ChainLds<D, Act> &L, OutRegs<D, Act> (&
     Ob = P * L.fac[cl & 1][2 * kC + 16 * a.wave + col];
     mcur[0] = C.mf[0];
     mcur[1] = C.mf[1];
-    out_issue<D, Act, 2>(R[(K + 2) % 3], a, cn, ws);
+    out_issue<D, Act, 2>(R[(K + NB - 1) % NB], a, cn, ws);
     __syncthreads();  // #2: dt complete
 
     // phase 3: beta * conv(v) of the next step
     if (cl + 1 < nsub) conv_bv<D, Act, SILU>(L, a, (cl + 1) & 1, w0, w1, w2, w3);
-    out_issue<D, Act, 1>(R[(K + 2) % 3], a, cn, ws);
+    out_issue<D, Act, 1>(R[(K + NB - 1) % NB], a, cn, ws);
     __syncthreads();  // #3: bv complete for the next step
 }
 
-template <int D, typename Act, typename Out, bool SILU>
-__global__ __launch_bounds__(512) void chain_kernel(SegArgs sa, const Act *__restrict__ x,
+// NB 3 fits one workgroup per CU (158 VGPRs at D = 128); NB 2 keeps every wave within 128 VGPRs
+// so that two workgroups share a CU, for launches with at least two workgroups per CU.
+template <int D, typename Act, typename Out, bool SILU, int NB>
+__global__ __launch_bounds__(512, NB == 2 ? 4 : 2) void chain_kernel(SegArgs sa, const Act *__restrict__ x,
                                                     const Act *__restrict__ conv_w, int conv_on,
                                                     int Hk, int Hv, float scale, Workspace ws,
                                                     Out *__restrict__ o)
@@ -888,12 +892,14 @@ __global__ __launch_bounds__(512) void chain_kernel(SegArgs sa, const Act *__res
                                              a.seg_n * Hv * D * (int)sizeof(Out), kRsrcWord3);
 
     if (state_role) {
-        StateRegs<D> R[3];
+        StateRegs<D> R[NB];
         if (nsub > 0) {
             state_issue<D, 1>(R[0], a, 0, ws);
             state_issue<D, 2>(R[0], a, 0, ws);
-            state_issue<D, 1>(R[1], a, min(1, nsub - 1), ws);
-            state_issue<D, 2>(R[1], a, min(1, nsub - 1), ws);
+            if constexpr (NB == 3) {
+                state_issue<D, 1>(R[1], a, min(1, nsub - 1), ws);
+                state_issue<D, 2>(R[1], a, min(1, nsub - 1), ws);
+            }
         }
         f32x4 S[TPW];
 #pragma unroll
@@ -910,16 +916,17 @@ __global__ __launch_bounds__(512) void chain_kernel(SegArgs sa, const Act *__res
         }
         __syncthreads();  // prologue #1
         __syncthreads();  // prologue #2
-        // Whole triples of steps first, with no exits inside: every load issued in the loop is
+        // Whole rounds of NB steps first, with no exits inside: every load issued in the loop is
         // then consumed on every path, and the compiler's waits stay behind the loads.
         int cl = 0;
-        for (; cl + 3 <= nsub; cl += 3) {
-            state_step<0, D, Act>(L, R, a, cl, nsub, S, ws);
-            state_step<1, D, Act>(L, R, a, cl + 1, nsub, S, ws);
-            state_step<2, D, Act>(L, R, a, cl + 2, nsub, S, ws);
+        for (; cl + NB <= nsub; cl += NB) {
+            state_step<0, NB, D, Act>(L, R, a, cl, nsub, S, ws);
+            state_step<1, NB, D, Act>(L, R, a, cl + 1, nsub, S, ws);
+            if constexpr (NB == 3) state_step<2, NB, D, Act>(L, R, a, cl + 2, nsub, S, ws);
         }
-        if (cl < nsub) state_step<0, D, Act>(L, R, a, cl, nsub, S, ws);
-        if (cl + 1 < nsub) state_step<1, D, Act>(L, R, a, cl + 1, nsub, S, ws);
+        if (cl < nsub) state_step<0, NB, D, Act>(L, R, a, cl, nsub, S, ws);
+        if constexpr (NB == 3)
+            if (cl + 1 < nsub) state_step<1, NB, D, Act>(L, R, a, cl + 1, nsub, S, ws);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int kt = wave * TPW + t;
@@ -937,30 +944,35 @@ __global__ __launch_bounds__(512) void chain_kernel(SegArgs sa, const Act *__res
             w2 = to_f32(conv_w[(a.vch + col) * 4 + 2]);
             w3 = to_f32(conv_w[(a.vch + col) * 4 + 3]);
         }
-        OutRegs<D, Act> R[3];
+        OutRegs<D, Act> R[NB];
         f32x4 Ob = {0.f, 0.f, 0.f, 0.f};
         half8 mcur[2] = {half8{}, half8{}};
         if (nsub > 0) {
             out_issue<D, Act, 3>(R[0], a, 0, ws);
             out_issue<D, Act, 3>(R[1], a, min(1, nsub - 1), ws);
-            out_issue<D, Act, 3>(R[2], a, min(2, nsub - 1), ws);
+            if constexpr (NB == 3) out_issue<D, Act, 3>(R[2], a, min(2, nsub - 1), ws);
             out_issue<D, Act, 1>(R[0], a, 0, ws);
             out_issue<D, Act, 2>(R[0], a, 0, ws);
-            out_issue<D, Act, 1>(R[1], a, min(1, nsub - 1), ws);
-            out_issue<D, Act, 2>(R[1], a, min(1, nsub - 1), ws);
+            if constexpr (NB == 3) {
+                out_issue<D, Act, 1>(R[1], a, min(1, nsub - 1), ws);
+                out_issue<D, Act, 2>(R[1], a, min(1, nsub - 1), ws);
+            }
             put_ld<D, Act>(L, R[0], a, 0, conv_on ? win : nullptr);
         }
         __syncthreads();  // prologue #1: raw v rows and factors of step 0 in LDS
         if (nsub > 0) conv_bv<D, Act, SILU>(L, a, 0, w0, w1, w2, w3);
         __syncthreads();  // prologue #2: bv of step 0 in LDS
         int cl = 0;
-        for (; cl + 3 <= nsub; cl += 3) {
-            out_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
-            out_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
-            out_step<2, D, Act, Out, SILU>(L, R, a, cl + 2, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+        for (; cl + NB <= nsub; cl += NB) {
+            out_step<0, NB, D, Act, Out, SILU>(L, R, a, cl, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+            out_step<1, NB, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+            if constexpr (NB == 3)
+                out_step<2, NB, D, Act, Out, SILU>(L, R, a, cl + 2, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
         }
-        if (cl < nsub) out_step<0, D, Act, Out, SILU>(L, R, a, cl, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
-        if (cl + 1 < nsub) out_step<1, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+        if (cl < nsub) out_step<0, NB, D, Act, Out, SILU>(L, R, a, cl, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
+        if constexpr (NB == 3)
+            if (cl + 1 < nsub)
+                out_step<1, NB, D, Act, Out, SILU>(L, R, a, cl + 1, nsub, Ob, mcur, w0, w1, w2, w3, scale, ws);
         // O of the last sub-chunk: its D^T was completed at the last step's barrier #2
         if (nsub > 0) out_store<D, Act, Out>(L, a, nsub - 1, Ob, mcur, scale);
     }
@@ -1239,6 +1251,18 @@ struct EventMarks {
     }
 };
 
+// The chain kernel's ring depth for a launch of n_wg workgroups: 2 (two workgroups per CU) once
+// there are at least two per CU, else 3.
+static bool chain_ring2(const gdn_desc &d, int64_t n_wg)
+{
+    (void)d;
+    int dev = 0, n_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return false;
+    return n_cu > 0 && n_wg >= 2 * (int64_t)n_cu;
+}
+
 template <int D, typename Act, typename Out>
 static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const void *conv_w,
                      const float *g, const float *beta, void *o, const Workspace &ws,
@@ -1256,14 +1280,27 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
                            d.n_v_heads, d.l2_eps, ws);
     em.mark(1);
     em.mark(2);
-    if (d.conv_silu && conv_on)
-        hipLaunchKernelGGL((chain_kernel<D, Act, Out, true>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
-                           dim3(512), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
-                           d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
-    else
-        hipLaunchKernelGGL((chain_kernel<D, Act, Out, false>), dim3((D / kTileV) * d.n_v_heads, sa.n_seg),
-                           dim3(512), 0, st, sa, (const Act *)x, (const Act *)conv_w, conv_on,
-                           d.n_k_heads, d.n_v_heads, d.scale, ws, (Out *)o);
+    const dim3 grid((D / kTileV) * d.n_v_heads, sa.n_seg);
+    const bool pair = chain_ring2(d, (int64_t)grid.x * grid.y);
+    if (d.conv_silu && conv_on) {
+        if (pair)
+            hipLaunchKernelGGL((chain_kernel<D, Act, Out, true, 2>), grid, dim3(512), 0, st, sa,
+                               (const Act *)x, (const Act *)conv_w, conv_on, d.n_k_heads,
+                               d.n_v_heads, d.scale, ws, (Out *)o);
+        else
+            hipLaunchKernelGGL((chain_kernel<D, Act, Out, true, 3>), grid, dim3(512), 0, st, sa,
+                               (const Act *)x, (const Act *)conv_w, conv_on, d.n_k_heads,
+                               d.n_v_heads, d.scale, ws, (Out *)o);
+    } else {
+        if (pair)
+            hipLaunchKernelGGL((chain_kernel<D, Act, Out, false, 2>), grid, dim3(512), 0, st, sa,
+                               (const Act *)x, (const Act *)conv_w, conv_on, d.n_k_heads,
+                               d.n_v_heads, d.scale, ws, (Out *)o);
+        else
+            hipLaunchKernelGGL((chain_kernel<D, Act, Out, false, 3>), grid, dim3(512), 0, st, sa,
+                               (const Act *)x, (const Act *)conv_w, conv_on, d.n_k_heads,
+                               d.n_v_heads, d.scale, ws, (Out *)o);
+    }
     em.mark(3);
     em.mark(4);  // the conv window is written by the chain kernel
     em.mark(5);

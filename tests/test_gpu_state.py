@@ -240,6 +240,50 @@ def test_branches_equal_full_prompt_prefill(b, desc):
         assert outs[k].pos == len(full)
 
 
+def test_batched_sequences_equal_single_calls(b, desc):
+    """Eight whole sequences of 1 to 16 sub-chunks (ragged and whole), from a zero state and
+    from a shared non-zero one, in one batched call: each equals its own single-sequence call
+    bit for bit, and the longest matches the oracle.  A batch of eight has 2,048 chain
+    workgroups at 32 value heads, so its chains run two workgroups per CU with a two-deep
+    prefetch ring; a single sequence has 256 and runs one per CU with a three-deep ring."""
+    lens = [64, 128, 192, 200, 256, 320, 1000, 1024]
+    total = 128 + sum(lens)
+    inp = synth.layer_inputs(SHAPE, total, seed=31)
+    dinp = to_dev(inp)
+    ws = b.workspace(desc, total, len(lens))
+    shared = b.State(desc)
+    run_fork(b, desc, dinp, new_state(b, desc), rows=(0, 128), out_state=shared, ws=ws)
+    zero = new_state(b, desc)
+    inits = [zero if k % 2 == 0 else shared for k in range(len(lens))]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    rows = slice(128, total)
+    o = torch.empty((cu[-1], 32, 128), dtype=torch.bfloat16, device="cuda")
+    outs = [b.State(desc) for _ in lens]
+    b.gdn_prefill_branches(desc, cu, dinp["x"][rows], dinp["conv_w"], dinp["g"][rows],
+                           dinp["beta"][rows], inits, outs, o, ws)
+    torch.cuda.synchronize()
+    for k, n in enumerate(lens):
+        r0 = 128 + cu[k]
+        of, sf = run_fork(b, desc, dinp, inits[k], rows=(r0, r0 + n), ws=ws)
+        torch.cuda.synchronize()
+        assert same_bits(o[cu[k]:cu[k + 1]], of), k
+        assert same_bits(outs[k].S, sf.S) and same_bits(outs[k].conv, sf.conv), k
+        assert outs[k].pos == inits[k].pos + n
+    k = 7  # 1,024 rows from the shared state
+    r0 = 128 + cu[k]
+    sub = {kk: v[r0:r0 + lens[k]] for kk, v in inp.items() if kk != "conv_w"}
+    sub["conv_w"] = inp["conv_w"]
+    o_ref, S_ref, w_ref = oracle(desc, sub, S0=shared.S.double().cpu().numpy(),
+                                 window=synth.f64(shared.conv.cpu()))
+    eo = rel_l2(o[cu[k]:cu[k + 1]].float().cpu().numpy(), o_ref)
+    es = rel_l2(outs[k].S.cpu().numpy(), S_ref)
+    print("batched 1024 rows from a shared state: rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
+    assert eo < TOL and es < TOL
+    assert np.array_equal(synth.f64(outs[k].conv.cpu()), w_ref)
+
+
 def test_refusals_enqueue_nothing(b, desc):
     dinp = to_dev(synth.layer_inputs(SHAPE, 128, seed=40))
     ws = b.workspace(desc, 128)
