@@ -82,6 +82,21 @@ def test_columns_are_invariant_to_the_tile_width(b, dtype):
     assert rel_l2(full.float().cpu().numpy(), _oracle(x, w)) < (FP32_TOL if dtype == torch.float32 else TOL)
 
 
+@pytest.mark.parametrize("K", [64, 128, 192, 256, 320, 384, 448, 512])
+def test_narrow_tiles_every_k_tail(b, K):
+    """The remainder tiles keep four K steps of 64 in flight; every count of K steps from one
+    to eight (each way the last round of four can end) against the oracle, and bit for bit
+    against the same columns in a 256-wide tile."""
+    T = 200
+    x, w = synth.linear_inputs(T, K, 320, seed=K)
+    xd, wd = x.cuda(), w.cuda()
+    full = _run(b, xd, wd, torch.float32)           # columns 256-319 in narrow tiles
+    wide = _run(b, xd, wd[64:].contiguous(), torch.float32)  # the same columns in a wide tile
+    torch.cuda.synchronize()
+    assert same_bits(wide[:, 192:], full[:, 256:])
+    assert rel_l2(full[:, 256:].cpu().numpy(), _oracle(x, w[256:])) < FP32_TOL
+
+
 def test_zero_rows_and_output_untouched_outside(b):
     x, w = synth.linear_inputs(8, 64, 32, seed=6)
     y = torch.full((8, 32), 7.0, dtype=torch.float32, device="cuda")
