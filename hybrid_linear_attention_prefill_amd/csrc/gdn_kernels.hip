@@ -1253,9 +1253,8 @@ struct EventMarks {
 
 // The chain kernel's ring depth for a launch of n_wg workgroups: 2 (two workgroups per CU) once
 // there are at least two per CU, else 3.
-static bool chain_ring2(const gdn_desc &d, int64_t n_wg)
+static bool chain_ring2(int64_t n_wg)
 {
-    (void)d;
     int dev = 0, n_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1281,7 +1280,7 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
     em.mark(1);
     em.mark(2);
     const dim3 grid((D / kTileV) * d.n_v_heads, sa.n_seg);
-    const bool pair = chain_ring2(d, (int64_t)grid.x * grid.y);
+    const bool pair = chain_ring2((int64_t)grid.x * grid.y);
     if (d.conv_silu && conv_on) {
         if (pair)
             hipLaunchKernelGGL((chain_kernel<D, Act, Out, true, 2>), grid, dim3(512), 0, st, sa,
