@@ -187,3 +187,41 @@ def test_fp32_activations_layer(b):
     o_ref, S_ref, w_ref = oracle(d, inp)
     _check_parity(o, s1.S, o_ref, S_ref)
     assert np.array_equal(synth.f64(s1.conv), w_ref)
+
+
+@pytest.mark.parametrize("shape,act,silu", [
+    (synth.Shape(8, 32, 64, 64, 4), torch.bfloat16, False),
+    (synth.Shape(16, 32, 128, 128, 4), torch.float32, False),
+    (synth.Shape(8, 32, 64, 64, 4), torch.float32, True),
+], ids=["d64_bf16", "d128_fp32", "d64_fp32_silu"])
+def test_batched_chain_instances_equal_single(b, shape, act, silu):
+    """A launch with at least two chain workgroups per CU runs the two-deep prefetch ring, one
+    sequence alone the three-deep one.  For head width 64, fp32 activations and SiLU: six
+    sequences of 1 to 5 sub-chunks (ragged and whole) in one batched call equal each run alone,
+    bit for bit, and one of them matches the oracle."""
+    d = _desc(b, shape, act=act, out=torch.float32, conv_silu=silu)
+    lens = [64, 100, 192, 256, 300, 320]
+    total = sum(lens)
+    inp = synth.layer_inputs(shape, total, seed=12, act_dtype=act)
+    dinp = to_dev(inp)
+    ws = b.workspace(d, total, len(lens))
+    zero = new_state(b, d)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    o = torch.empty((total, shape.n_v_heads, shape.d_v), dtype=torch.float32, device="cuda")
+    outs = [b.State(d) for _ in lens]
+    b.gdn_prefill_branches(d, cu, dinp["x"], dinp["conv_w"], dinp["g"], dinp["beta"],
+                           [zero] * len(lens), outs, o, ws)
+    torch.cuda.synchronize()
+    for k, n in enumerate(lens):
+        of, sf = run_fork(b, d, dinp, zero, rows=(cu[k], cu[k + 1]), ws=ws)
+        torch.cuda.synchronize()
+        assert same_bits(o[cu[k]:cu[k + 1]], of), k
+        assert same_bits(outs[k].S, sf.S) and same_bits(outs[k].conv, sf.conv), k
+    k = 4  # 300 rows: four whole sub-chunks and a ragged one
+    sub = {kk: v[cu[k]:cu[k + 1]] for kk, v in inp.items() if kk != "conv_w"}
+    sub["conv_w"] = inp["conv_w"]
+    o_ref, S_ref, w_ref = oracle(d, sub)
+    _check_parity(o[cu[k]:cu[k + 1]], outs[k].S, o_ref, S_ref)
+    assert np.array_equal(synth.f64(outs[k].conv), w_ref)
