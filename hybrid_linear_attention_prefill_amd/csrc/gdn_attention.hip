@@ -42,14 +42,29 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 3;
 
-// An LDS block holds 64 key rows of D bf16, each row padded by one 16-byte chunk: chunk c of
-// row t sits at 16-byte slot t (D / 8 + 1) + c, so rows t and t + 1 start one chunk apart
-// (mod the 256-byte bank window) and every fragment address is one per-lane base plus a
+// An LDS block holds 64 key rows of D bf16 (R = D / 8 chunks of 16 bytes per row), in one of two
+// layouts of the same size; in both, every fragment address is one per-lane base plus a
 // compile-time offset.
+//  - V blocks: each row padded by one chunk, chunk c of row t at slot t (R + 1) + c, so rows t
+//    and t + 1 start one chunk apart in the 256-byte bank window (the transposed reads below).
+//  - K blocks: rows in pairs, chunk c of row t at slot (t / 2)(2 R + 2) + (t mod 2) R + c, so
+//    rows 2 s and 2 s + 1 start at the same even chunk of the window and consecutive pairs two
+//    chunks apart.  A 16-byte read serves its 64 lanes in four passes of 16, lanes 0-7 with
+//    24-31 and 8-15 with 16-23 (and the same in the upper half): in a K fragment read those
+//    are 8 even keys of one d-chunk with 8 odd keys of the next, which then fill the 16
+//    chunk slots of the window.  (With padded rows an even and an odd key row meet in the same
+//    slot: two-way conflicts, half of the LDS cycles of the reads.)
 template <int D>
 constexpr int kRowChunks = D / 8 + 1;
 template <int D>
 constexpr int kSlotChunks = kBlk * kRowChunks<D>;
+template <int D>
+constexpr int kPairChunks = 2 * (D / 8) + 2;  // one pair of K rows
+template <int D>
+__device__ __forceinline__ int k_row_start(int t)
+{
+    return (t >> 1) * kPairChunks<D> + (t & 1) * (D / 8);
+}
 
 // Key order inside a 16-key MFMA tile: row r of the tile is key sigma(r) = 2 (r mod 8) + r / 8.
 // With it the 16 rows of a K fragment read have distinct residues mod 16 (no bank conflict),
@@ -87,22 +102,22 @@ __device__ __forceinline__ void blk_load(const uint16_t *base, int64_t key0, int
 }
 
 template <int D>
-__device__ __forceinline__ void blk_store(u32x4 *slot, int tid, const u32x4 (&v)[D / 64])
+__device__ __forceinline__ void blk_store(u32x4 *slot, int tid, const u32x4 (&v)[D / 64], bool isv)
 {
 #pragma unroll
     for (int i = 0; i < D / 64; ++i) {
         const int id = tid + kThreads * i, row = id / (D / 8), pc = id % (D / 8);
-        slot[row * kRowChunks<D> + pc] = v[i];
+        slot[(isv ? row * kRowChunks<D> : k_row_start<D>(row)) + pc] = v[i];
     }
 }
 
 // K fragment (A operand of S^T = K Q^T) for tile q4 and d-step ks: lane (r = lane % 16, g)
 // holds K[16 q4 + sigma(r)][32 ks + 8 g .. + 7].  kbase = the lane's slot offset of
-// (sigma(r), g).
+// (sigma(r), g) in the paired-row layout; 16 rows are 8 pairs.
 template <int D>
 __device__ __forceinline__ bf16x8 k_frag(const u32x4 *slot, int kbase, int q4, int ks)
 {
-    return __builtin_bit_cast(bf16x8, slot[kbase + 16 * q4 * kRowChunks<D> + 4 * ks]);
+    return __builtin_bit_cast(bf16x8, slot[kbase + 8 * q4 * kPairChunks<D> + 4 * ks]);
 }
 
 // V^T fragment (A operand of O^T = V^T P^T) for output columns 16 ct .. + 15 and the 32 keys
@@ -190,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     const uint16_t *kp = (const uint16_t *)sq.k, *vp = (const uint16_t *)sq.v;
     uint32_t boff[D / 64];
     blk_offsets<D>(Hkv, kvh, tid, boff);
-    const int kbase = sigma(li) * kRowChunks<D> + g;
+    const int kbase = k_row_start<D>(sigma(li)) + g;
     const int j4 = lane & 15;
     const int vbase = 16 * sigma(4 * g + j4 / 4) * kRowChunks<D> + 8 * (j4 % 4);
 
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     for (int b = 0; b < 2; ++b) {
         if (ld.j < ns) {
             blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, boff, stage);
-            blk_store<D>(ring[b], tid, stage);
+            blk_store<D>(ring[b], tid, stage, ld.isv != 0);
             advance(ld, ns, nk_last);
         }
     }
@@ -236,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
             blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, boff, stage);
         work(ring[rs]);
         if (more) {
-            blk_store<D>(ring[rs == 0 ? 2 : rs - 1], tid, stage);
+            blk_store<D>(ring[rs == 0 ? 2 : rs - 1], tid, stage, ld.isv != 0);
             advance(ld, ns, nk_last);
         }
         __syncthreads();
