@@ -577,6 +577,9 @@ struct OutRegs {
     static constexpr int EPC = 16 / (int)sizeof(Act);
     static constexpr int VCR = 16 / EPC;               // chunks per v row (16 values)
     static constexpr int VC = (kC + 3) * VCR;          // v chunks
+    // In LDS each raw v row takes one chunk more than its 16 values: the conv's 2- or 4-byte
+    // reads of rows 4 apart then fall in different banks (without the pad they meet two ways).
+    static constexpr int VRS = VCR + 1;
     static constexpr int NLD = VC + 64;                // + factor table chunks
     static constexpr int LP = (NLD + 255) / 256;       // chunks per output thread
     half8 qf[KB], mf[2];
@@ -655,7 +658,7 @@ struct ChainLds {
     _Float16 s16t[16 * RW];                // S^T, fp16: the B operand of X and P
     _Float16 rt[16 * RW], dt[16 * RW], ddt[16 * RW];  // R^T, D^T, (exp(G_n - G) D)^T
     float bv[16 * BS];                     // beta * conv(v) of the next step, [column][row]
-    u32x4 xvr[OutRegs<D, Act>::VC];        // raw v rows of the next step (3 halo rows + 64)
+    u32x4 xvr[(kC + 3) * OutRegs<D, Act>::VRS];  // raw v rows of the next step (3 halo rows + 64)
     float fac[2][4 * kC];                  // per row: beta, beta*gamma, gamma, exp(G_n - G)
 };
 
@@ -673,11 +676,10 @@ __device__ __forceinline__ void put_ld(ChainLds<D, Act> &L, const OutRegs<D, Act
         const int idx = a.ot + 256 * i;
         u32x4 v = R.ld[i];
         if (idx < OR::VC) {
-            if (win != nullptr && idx < 3 * OR::VCR) {
-                const int vr = idx / OR::VCR, cc = (idx % OR::VCR) * OR::EPC;
-                v = v | *(const u32x4 *)(win + (int64_t)vr * a.C + a.vch + cc);
-            }
-            L.xvr[idx] = v;
+            const int vr = idx / OR::VCR, ci = idx % OR::VCR;
+            if (win != nullptr && idx < 3 * OR::VCR)
+                v = v | *(const u32x4 *)(win + (int64_t)vr * a.C + a.vch + ci * OR::EPC);
+            L.xvr[vr * OR::VRS + ci] = v;
         } else if (idx < OR::NLD) {
             ((u32x4 *)L.fac[buf])[idx - OR::VC] = v;
         }
@@ -692,10 +694,11 @@ __device__ __forceinline__ void conv_bv(ChainLds<D, Act> &L, const ChainArgs &a,
 {
     using CL = ChainLds<D, Act>;
     const int r0 = 16 * a.wave + 4 * a.kg;
+    constexpr int RS = OutRegs<D, Act>::VRS * OutRegs<D, Act>::EPC;  // row stride, in values
     const Act *vrows = (const Act *)L.xvr;
     float vr[7];
 #pragma unroll
-    for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * 16 + a.col]);
+    for (int j = 0; j < 7; ++j) vr[j] = to_f32(vrows[(r0 + j) * RS + a.col]);
     const f32x4 fb = *(const f32x4 *)(L.fac[buf] + r0);
     f32x4 bvv;
 #pragma unroll
