@@ -8,7 +8,6 @@ fallback.
 """
 import ctypes
 import os
-import re
 
 import torch
 
@@ -16,141 +15,49 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn_prefill.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
-GDN_OK, GDN_EINVAL, GDN_ESHAPE, GDN_EGRID = 0, -1, -2, -3
-GDN_EMISMATCH, GDN_EWORKSPACE, GDN_EDEVICE, GDN_EALIAS, GDN_EFILE = -4, -5, -6, -7, -8
-GDN_F32, GDN_BF16 = 0, 1
-GDN_COMMIT, GDN_FORK = 0, 1
-SUB_CHUNK = 64
-MAX_CHECKPOINTS = 6
+from .abi import (GDN_OK, GDN_EINVAL, GDN_ESHAPE, GDN_EGRID, GDN_EMISMATCH,  # noqa: F401
+                  GDN_EWORKSPACE, GDN_EDEVICE, GDN_EALIAS, GDN_EFILE, GDN_F32, GDN_BF16,
+                  GDN_COMMIT, GDN_FORK, SUB_CHUNK, MAX_CHECKPOINTS, gdn_desc, gdn_state,
+                  gdn_attn_desc, gdn_attn_seq, gdn_ckpt_ring, dtype_code, GDN_STORE_UNUSED,
+                  GDN_STORE_RESIDENT, GDN_STORE_ON_DISK, GDN_STORE_DROPPED,
+                  GDN_STORE_WAS_RESIDENT, GDN_STORE_FROM_DISK, GDN_STORE_FRESH)
+from . import abi as _abi
 
 _DTYPE_CODE = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
-_CODE_DTYPE = {GDN_F32: torch.float32, GDN_BF16: torch.bfloat16}
 
 
-class GdnError(RuntimeError):
-    def __init__(self, status, where):
-        self.status = status
-        super().__init__("%s: %s (%d)" % (where, gdn_status_str(status), status))
-
-
-class gdn_desc(ctypes.Structure):
-    _fields_ = [("n_k_heads", ctypes.c_int32), ("n_v_heads", ctypes.c_int32),
-                ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
-                ("conv_width", ctypes.c_int32), ("sub_chunk", ctypes.c_int32),
-                ("grid", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("conv_silu", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("l2_eps", ctypes.c_float)]
-
-    @property
-    def channels(self):
-        return 2 * self.n_k_heads * self.d_k + self.n_v_heads * self.d_v
-
-    @property
-    def act_torch(self):
-        return _CODE_DTYPE[self.act_dtype]
-
-    @property
-    def out_torch(self):
-        return _CODE_DTYPE[self.out_dtype]
-
-
-class gdn_state(ctypes.Structure):
-    _fields_ = [("S", ctypes.c_void_p), ("conv", ctypes.c_void_p), ("pos", ctypes.c_int64),
-                ("tag", ctypes.c_uint64)]
-
-
-class gdn_attn_desc(ctypes.Structure):
-    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
-
-    @property
-    def out_torch(self):
-        return _CODE_DTYPE[self.out_dtype]
-
-
-class gdn_attn_seq(ctypes.Structure):
-    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
-                ("o", ctypes.c_void_p), ("pos0", ctypes.c_int64), ("T", ctypes.c_int64)]
-
-
-class gdn_ckpt_ring(ctypes.Structure):
-    _fields_ = [("cap", ctypes.c_int32), ("n", ctypes.c_int32),
-                ("pos", ctypes.c_int64 * MAX_CHECKPOINTS),
-                ("age", ctypes.c_uint64 * MAX_CHECKPOINTS), ("clock", ctypes.c_uint64)]
+GdnError = _abi.GdnError
 
 
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError("libgdn_prefill.so is not built: run "
                           "python -m hybrid_linear_attention_prefill_amd.build")
-    lib = ctypes.CDLL(LIB_PATH)
-    D, S, V, I32, I64, SZ = (ctypes.POINTER(gdn_desc), ctypes.POINTER(gdn_state), ctypes.c_void_p,
-                            ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t)
-    R = ctypes.POINTER(gdn_ckpt_ring)
-    sig = {
-        "gdn_desc_check": (I32, [D]),
-        "gdn_desc_tag": (ctypes.c_uint64, [D]),
-        "gdn_state_S_bytes": (SZ, [D]),
-        "gdn_state_conv_bytes": (SZ, [D]),
-        "gdn_workspace_bytes": (SZ, [D, I64, I32]),
-        "gdn_state_init": (I32, [D, S, V]),
-        "gdn_state_capture": (I32, [D, S, S, V]),
-        "gdn_state_restore": (I32, [D, S, S, V]),
-        "gdn_state_fork": (I32, [D, S, S, I32, V]),
-        "conv1d_state_step": (I32, [D, V, V, V, V, I64, V]),
-        "gdn_prefill_chunked": (I32, [D, V, V, V, V, S, S, V, I64, I32,
-                                      ctypes.POINTER(ctypes.c_int64), V, SZ, V]),
-        "gdn_prefill_chunked_events": (I32, [D, V, V, V, V, S, S, V, I64, I32,
-                                             ctypes.POINTER(ctypes.c_int64), V, SZ, V,
-                                             ctypes.POINTER(ctypes.c_void_p), I32]),
-        "gdn_prefill_branches": (I32, [D, I32, ctypes.POINTER(ctypes.c_int64), V, V, V, V,
-                                       ctypes.POINTER(S), ctypes.POINTER(S), V, V, SZ, V]),
-        "gdn_decode_step": (I32, [D, I32, V, V, V, V, ctypes.POINTER(S), ctypes.POINTER(S), V, V]),
-        "gdn_state_file_header_bytes": (SZ, []),
-        "gdn_state_file_write": (I32, [D, V, V, I64, ctypes.c_uint64, ctypes.c_char_p]),
-        "gdn_state_file_read": (I32, [D, V, V, ctypes.POINTER(ctypes.c_int64), ctypes.c_uint64,
-                                      ctypes.c_char_p]),
-        "gdn_state_save": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
-        "gdn_state_load": (I32, [D, S, ctypes.c_uint64, ctypes.c_char_p, V]),
-        "gdn_linear": (I32, [I64, I32, I32, V, V, V, I32, V]),
-        "gdn_attention_prefill": (I32, [ctypes.POINTER(gdn_attn_desc), I32,
-                                        ctypes.POINTER(gdn_attn_seq), V]),
-        "gdn_commit_rows": (I64, [I64, I32]),
-        "gdn_shared_prefix_rows": (I64, [I64, I64]),
-        "gdn_ckpt_init": (I32, [R, I32]),
-        "gdn_ckpt_push": (I32, [R, I64]),
-        "gdn_ckpt_find": (I32, [R, I64]),
-        "gdn_ckpt_drop_above": (I32, [R, I64]),
-        "gdn_status_str": (ctypes.c_char_p, [I32]),
-    }
-    for name, (res, args) in sig.items():
-        f = getattr(lib, name)
-        f.restype, f.argtypes = res, args
-    return lib
+    return _abi.declare(ctypes.CDLL(LIB_PATH))
 
 
 lib = _load()
+_host = _abi.HostCalls(lib)
+# host-only calls (no device memory): descriptor, sizes, grid arithmetic, checkpoint ring,
+# state files in host buffers
+gdn_status_str = _host.gdn_status_str
+_check = _host.check
+gdn_desc_check = _host.gdn_desc_check
+gdn_desc_tag = _host.gdn_desc_tag
+gdn_state_S_bytes = _host.gdn_state_S_bytes
+gdn_state_conv_bytes = _host.gdn_state_conv_bytes
+gdn_workspace_bytes = _host.gdn_workspace_bytes
+gdn_state_file_header_bytes = _host.gdn_state_file_header_bytes
+gdn_state_file_write = _host.gdn_state_file_write
+gdn_state_file_read = _host.gdn_state_file_read
+gdn_commit_rows = _host.gdn_commit_rows
+gdn_shared_prefix_rows = _host.gdn_shared_prefix_rows
+CkptRing = _host.CkptRing
 
 
 def exported_names():
     """Function names declared in include/gdn.h (for the ABI tests)."""
-    names = []
-    with open(HEADER) as f:
-        for line in f:
-            m = re.match(r"^(?:const\s+)?[A-Za-z_]\w*\s*\*?\s*([A-Za-z_]\w*)\s*\(", line)
-            if m:
-                names.append(m.group(1))
-    return names
-
-
-def gdn_status_str(status):
-    return lib.gdn_status_str(int(status)).decode()
-
-
-def _check(status, where):
-    if status != GDN_OK:
-        raise GdnError(status, where)
+    return _abi.declared_names(HEADER)
 
 
 def _ptr(t):
@@ -174,30 +81,9 @@ def _stream(stream):
 def make_desc(n_k_heads, n_v_heads, d_k, d_v, *, conv_width=4, grid=512,
               act_dtype=torch.bfloat16, out_dtype=torch.bfloat16, conv_silu=False, scale=None,
               l2_eps=1e-6, sub_chunk=SUB_CHUNK):
-    d = gdn_desc(n_k_heads, n_v_heads, d_k, d_v, conv_width, sub_chunk, grid,
-                 _DTYPE_CODE[act_dtype], _DTYPE_CODE[out_dtype], 1 if conv_silu else 0,
-                 float(d_k ** -0.5 if scale is None else scale), float(l2_eps))
-    return d
-
-
-def gdn_desc_check(desc):
-    return lib.gdn_desc_check(ctypes.byref(desc))
-
-
-def gdn_desc_tag(desc):
-    return lib.gdn_desc_tag(ctypes.byref(desc))
-
-
-def gdn_state_S_bytes(desc):
-    return lib.gdn_state_S_bytes(ctypes.byref(desc))
-
-
-def gdn_state_conv_bytes(desc):
-    return lib.gdn_state_conv_bytes(ctypes.byref(desc))
-
-
-def gdn_workspace_bytes(desc, max_rows, max_segments=1):
-    return lib.gdn_workspace_bytes(ctypes.byref(desc), int(max_rows), int(max_segments))
+    return _abi.make_desc(n_k_heads, n_v_heads, d_k, d_v, conv_width=conv_width, grid=grid,
+                          act_dtype=act_dtype, out_dtype=out_dtype, conv_silu=conv_silu,
+                          scale=scale, l2_eps=l2_eps, sub_chunk=sub_chunk)
 
 
 class State:
@@ -310,37 +196,6 @@ def gdn_decode_step(desc, x, conv_w, g, beta, inits, outs, o, stream=None):
     _check(st, "gdn_decode_step")
 
 
-def gdn_state_file_header_bytes():
-    return lib.gdn_state_file_header_bytes()
-
-
-def _np_ptr(a):
-    return None if a is None else a.ctypes.data
-
-
-def gdn_state_file_write(desc, S_host, conv_host, pos, weights_hash, path):
-    """Host-buffer form: S_host [Hv][d_k][d_v] float32 and conv_host [W-1][C] numpy arrays of
-    the activation dtype's bytes (float32, or uint16 holding bf16 bits)."""
-    _check(lib.gdn_state_file_write(ctypes.byref(desc), _np_ptr(S_host), _np_ptr(conv_host),
-                                    int(pos), int(weights_hash), os.fsencode(path)),
-           "gdn_state_file_write")
-
-
-def gdn_state_file_read(desc, weights_hash, path):
-    """Returns (S [Hv][d_k][d_v] float32, window as raw numpy (float32 or uint16) or None, pos)."""
-    import numpy as np
-    S = np.empty((desc.n_v_heads, desc.d_k, desc.d_v), dtype=np.float32)
-    conv = None
-    if desc.conv_width > 0:
-        conv = np.empty((desc.conv_width - 1, desc.channels),
-                        dtype=np.uint16 if desc.act_dtype == GDN_BF16 else np.float32)
-    pos = ctypes.c_int64(-1)
-    _check(lib.gdn_state_file_read(ctypes.byref(desc), _np_ptr(S), _np_ptr(conv),
-                                   ctypes.byref(pos), int(weights_hash), os.fsencode(path)),
-           "gdn_state_file_read")
-    return S, conv, pos.value
-
-
 def gdn_state_save(desc, state, weights_hash, path, stream=None):
     _check(lib.gdn_state_save(ctypes.byref(desc), state.ref(), int(weights_hash),
                               os.fsencode(path), _stream(stream)), "gdn_state_save")
@@ -360,7 +215,7 @@ def gdn_linear(x, w, y, stream=None):
 
 
 def make_attn_desc(n_q_heads, n_kv_heads, head_dim, *, out_dtype=torch.bfloat16, scale=None):
-    return gdn_attn_desc(n_q_heads, n_kv_heads, head_dim, _DTYPE_CODE[out_dtype],
+    return gdn_attn_desc(n_q_heads, n_kv_heads, head_dim, dtype_code(out_dtype),
                          float(head_dim ** -0.5 if scale is None else scale))
 
 
@@ -373,29 +228,26 @@ def gdn_attention_prefill(desc, seqs, stream=None):
            "gdn_attention_prefill")
 
 
-def gdn_commit_rows(n, grid):
-    return lib.gdn_commit_rows(int(n), int(grid))
+class SessionStore(_abi.Store):
+    """gdn_store over n_slots device states made here; acquire() returns (State, origin) and
+    raises GdnError on failure."""
 
+    def __init__(self, desc, n_slots, cap_bytes, directory=None, weights_hash=0, max_entries=None,
+                 device="cuda"):
+        super().__init__(lib, desc, [State(desc, device=device) for _ in range(n_slots)], cap_bytes,
+                         directory, weights_hash, max_entries)
+        _check(self.status, "gdn_store_init")
 
-def gdn_shared_prefix_rows(state_pos, prefix_end):
-    return lib.gdn_shared_prefix_rows(int(state_pos), int(prefix_end))
+    def acquire(self, sid, stream=None):
+        st, slot, origin = super().acquire(sid, _stream(stream))
+        _check(st, "gdn_store_acquire")
+        return slot, origin
 
+    def evict(self, sid, stream=None):
+        _check(super().evict(sid, _stream(stream)), "gdn_store_evict")
 
-class CkptRing:
-    """The library's checkpoint ring (host only)."""
+    def flush(self, stream=None):
+        _check(super().flush(_stream(stream)), "gdn_store_flush")
 
-    def __init__(self, cap=MAX_CHECKPOINTS):
-        self.c = gdn_ckpt_ring()
-        _check(lib.gdn_ckpt_init(ctypes.byref(self.c), int(cap)), "gdn_ckpt_init")
-
-    def push(self, pos):
-        return lib.gdn_ckpt_push(ctypes.byref(self.c), int(pos))
-
-    def find(self, d):
-        return lib.gdn_ckpt_find(ctypes.byref(self.c), int(d))
-
-    def drop_above(self, d):
-        return lib.gdn_ckpt_drop_above(ctypes.byref(self.c), int(d))
-
-    def positions(self):
-        return [self.c.pos[i] for i in range(self.c.cap)]
+    def drop(self, sid):
+        _check(super().drop(sid), "gdn_store_drop")

@@ -2,7 +2,8 @@
 
     python -m hybrid_linear_attention_prefill_amd.build
 
-Compiles csrc/gdn_host.cpp (validation, scheduling, launches), csrc/gdn_kernels.hip (the
+Compiles csrc/gdn_host.cpp (validation, scheduling, launches), csrc/gdn_store.cpp (the session
+store), csrc/gdn_kernels.hip (the
 layer's kernels), csrc/gdn_linear.hip (the projection GEMM) and csrc/gdn_attention.hip (the
 full-attention layers) into libgdn_prefill.so beside this file.  Always recompiles.
 """
@@ -13,7 +14,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn_prefill.so")
-SOURCES = [os.path.join(PKG, "csrc", "gdn_host.cpp"), os.path.join(PKG, "csrc", "gdn_kernels.hip"),
+SOURCES = [os.path.join(PKG, "csrc", "gdn_host.cpp"), os.path.join(PKG, "csrc", "gdn_store.cpp"),
+           os.path.join(PKG, "csrc", "gdn_kernels.hip"),
            os.path.join(PKG, "csrc", "gdn_linear.hip"), os.path.join(PKG, "csrc", "gdn_attention.hip")]
 ARCH = "gfx950"
 

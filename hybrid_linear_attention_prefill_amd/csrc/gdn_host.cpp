@@ -1,10 +1,9 @@
 // gdn_host.cpp -- host half of libgdn_prefill.so: argument validation, the commit-grid
-// arithmetic, state copies and the launch sequence.  Every check runs before the first HIP
+// arithmetic, state copies and the launch sequence.  It includes no ROCm header: the device
+// is reached only through the launch_* functions of gdn_internal.h.  Every check runs before the first HIP
 // call, so a refused call enqueues nothing and changes no state (the pages refuse invalid
 // requests before any device work: PR "qwen3_5: run prompts that share prefixes once per
 // prefix", sections "Test Plan" and "Test Result").
-#include <hip/hip_runtime.h>
-
 #include <unistd.h>
 
 #include <algorithm>
@@ -13,6 +12,7 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -44,10 +44,10 @@ Workspace carve_workspace(const gdn_desc &d, int64_t n_sub, void *base)
     const size_t tm = align256((size_t)n_sub * d.n_v_heads * kPackedTri * 2);
     char *p = (char *)base;
     Workspace w;
-    w.Qh = (_Float16 *)p;
-    w.Kh = (_Float16 *)(p + qk);
-    w.Tm = (_Float16 *)(p + 2 * qk);
-    w.Mm = (_Float16 *)(p + 2 * qk + tm);
+    w.Qh = (uint16_t *)p;
+    w.Kh = (uint16_t *)(p + qk);
+    w.Tm = (uint16_t *)(p + 2 * qk);
+    w.Mm = (uint16_t *)(p + 2 * qk + tm);
     w.Fac = (float *)(p + 2 * qk + 2 * tm);
     return w;
 }
@@ -136,6 +136,15 @@ static gdn_status check_state(const gdn_desc &d, const gdn_state *s)
     return GDN_OK;
 }
 
+// A state the library writes (init, capture, restore, fork targets): the copy and zero kernels
+// move S in 4-byte words and the window in 16-byte pieces.
+static gdn_status check_dst(const gdn_desc &d, const gdn_state *s)
+{
+    if (!s || !s->S || !aligned(s->S, 4)) return GDN_EINVAL;
+    if (d.conv_width > 0 && (!s->conv || !aligned(s->conv, 16))) return GDN_EINVAL;
+    return GDN_OK;
+}
+
 static gdn_status copy_state(const gdn_desc &d, const gdn_state *src, gdn_state *dst, void *stream)
 {
     if (launch_copy(dst->S, src->S, gdn_state_S_bytes(&d), stream) != 0) return GDN_EDEVICE;
@@ -177,12 +186,21 @@ static gdn_status run_segments(const gdn_desc &d, const std::vector<Seg> &segs, 
 // Rows of one sequence per launch: the chain kernel addresses x and o of a sequence with 32-bit
 // byte offsets, so a longer sequence is run as several chained launches, each starting at a
 // multiple of 64 rows (which changes no bit of the result).
+// The environment variable GDN_TEST_LAUNCH_ROWS (a positive multiple of 64) lowers the cap, so
+// that tests can run the chained-launch path at small sizes; it is read on every call and never
+// raises the cap.
 static int64_t max_rows_per_launch(const gdn_desc &d)
 {
     const int64_t row_bytes = std::max<int64_t>(n_channels(d) * (int64_t)act_size(d),
                                                 (int64_t)d.n_v_heads * d.d_v * (int64_t)out_size(d));
     const int64_t rows = ((int64_t)INT32_MAX - 4 * row_bytes) / row_bytes;
-    return (rows / kC) * kC;
+    int64_t cap = (rows / kC) * kC;
+    if (const char *e = std::getenv("GDN_TEST_LAUNCH_ROWS")) {
+        char *end = nullptr;
+        const long long v = std::strtoll(e, &end, 10);
+        if (end != e && *end == '\0' && v > 0 && v % kC == 0 && v < cap) cap = v;
+    }
+    return cap;
 }
 
 // Largest per-launch sub-chunk count of `segs`.
@@ -329,6 +347,10 @@ gdn_status gdn_desc_check(const gdn_desc *d)
     if (d->sub_chunk != GDN_SUB_CHUNK) return GDN_ESHAPE;
     if (d->grid <= 0 || d->grid % GDN_SUB_CHUNK != 0) return GDN_ESHAPE;
     if (n_channels(*d) > (int64_t)1 << 24) return GDN_ESHAPE;
+    // a launch must hold at least one sub-chunk of rows (x and o offsets are 32-bit)
+    const int64_t row_bytes = std::max<int64_t>(n_channels(*d) * (int64_t)act_size(*d),
+                                                (int64_t)d->n_v_heads * d->d_v * (int64_t)out_size(*d));
+    if (((int64_t)INT32_MAX - 4 * row_bytes) / row_bytes < kC) return GDN_ESHAPE;
     return GDN_OK;
 }
 
@@ -358,17 +380,25 @@ size_t gdn_state_conv_bytes(const gdn_desc *d)
     return (size_t)(d->conv_width - 1) * n_channels(*d) * act_size(*d);
 }
 
+// Bytes of the scratch final states a branch batch without requested final states writes:
+// one S and window per sequence of a launch.
+static size_t scratch_states_bytes(const gdn_desc &d, int64_t n_seq)
+{
+    const size_t one = align256(gdn_state_S_bytes(&d)) + align256(gdn_state_conv_bytes(&d));
+    return (size_t)std::min<int64_t>(n_seq, kMaxSegPerLaunch) * one;
+}
+
 size_t gdn_workspace_bytes(const gdn_desc *d, int64_t max_rows, int32_t max_segments)
 {
     if (gdn_desc_check(d) != GDN_OK || max_rows < 0 || max_segments < 0) return 0;
-    return workspace_bytes(*d, max_rows / kC + max_segments);
+    return workspace_bytes(*d, max_rows / kC + max_segments) + scratch_states_bytes(*d, max_segments);
 }
 
 gdn_status gdn_state_init(const gdn_desc *d, gdn_state *s, void *stream)
 {
     gdn_status st = gdn_desc_check(d);
     if (st) return st;
-    if (!s || !s->S || (d->conv_width > 0 && !s->conv)) return GDN_EINVAL;
+    if ((st = check_dst(*d, s))) return st;
     if (launch_zero(s->S, gdn_state_S_bytes(d), stream) != 0) return GDN_EDEVICE;
     if (d->conv_width > 0 && launch_zero(s->conv, gdn_state_conv_bytes(d), stream) != 0)
         return GDN_EDEVICE;
@@ -383,7 +413,7 @@ gdn_status gdn_state_capture(const gdn_desc *d, const gdn_state *live, gdn_state
     gdn_status st = gdn_desc_check(d);
     if (st) return st;
     if ((st = check_state(*d, live))) return st;
-    if (!snap || !snap->S || (d->conv_width > 0 && !snap->conv)) return GDN_EINVAL;
+    if ((st = check_dst(*d, snap))) return st;
     if (states_overlap(*d, live, snap)) return GDN_EALIAS;
     if ((st = copy_state(*d, live, snap, stream))) return st;
     snap->pos = live->pos;
@@ -397,7 +427,7 @@ gdn_status gdn_state_restore(const gdn_desc *d, gdn_state *live, const gdn_state
     gdn_status st = gdn_desc_check(d);
     if (st) return st;
     if ((st = check_state(*d, snap))) return st;
-    if (!live || !live->S || (d->conv_width > 0 && !live->conv)) return GDN_EINVAL;
+    if ((st = check_dst(*d, live))) return st;
     if (states_overlap(*d, live, snap)) return GDN_EALIAS;
     if ((st = copy_state(*d, snap, live, stream))) return st;
     live->pos = snap->pos;
@@ -413,7 +443,7 @@ gdn_status gdn_state_fork(const gdn_desc *d, const gdn_state *src, gdn_state *ds
     if ((st = check_state(*d, src))) return st;
     if (n < 0 || (n > 0 && !dst)) return GDN_EINVAL;
     for (int32_t i = 0; i < n; ++i) {
-        if (!dst[i].S || (d->conv_width > 0 && !dst[i].conv)) return GDN_EINVAL;
+        if ((st = check_dst(*d, &dst[i]))) return st;
         if (states_overlap(*d, src, &dst[i])) return GDN_EALIAS;
         for (int32_t j = 0; j < i; ++j)
             if (states_overlap(*d, &dst[i], &dst[j])) return GDN_EALIAS;
@@ -569,7 +599,7 @@ gdn_status gdn_prefill_branches(const gdn_desc *d, int32_t B, const int64_t *cu_
     const int64_t subs = max_launch_subs(segs);
     size_t need = workspace_bytes(*d, subs);
     const size_t s_bytes = gdn_state_S_bytes(d), c_bytes = align256(gdn_state_conv_bytes(d));
-    if (!out) need += (size_t)std::min<int32_t>(B, kMaxSegPerLaunch) * (align256(s_bytes) + c_bytes);
+    if (!out) need += scratch_states_bytes(*d, B);
     if (!ws || ws_bytes < need) return GDN_EWORKSPACE;
     if (!aligned(ws, 16)) return GDN_EINVAL;
     if (io_overlap(*d, cu_rows[B], x, conv_w, g, beta, o, ws, need, init, B,
@@ -703,10 +733,8 @@ gdn_status gdn_state_save(const gdn_desc *d, const gdn_state *state, uint64_t we
     if (!path || !*path) return GDN_EINVAL;
     const size_t sb = gdn_state_S_bytes(d), cb = gdn_state_conv_bytes(d);
     std::vector<unsigned char> host(sb + cb);
-    hipStream_t hs = (hipStream_t)stream;
-    if (hipMemcpyAsync(host.data(), state->S, sb, hipMemcpyDeviceToHost, hs) != hipSuccess ||
-        (cb && hipMemcpyAsync(host.data() + sb, state->conv, cb, hipMemcpyDeviceToHost, hs) != hipSuccess) ||
-        hipStreamSynchronize(hs) != hipSuccess)
+    if (copy_to_host(host.data(), state->S, sb, stream) != 0 ||
+        (cb && copy_to_host(host.data() + sb, state->conv, cb, stream) != 0) || stream_sync(stream) != 0)
         return GDN_EDEVICE;
     return write_state_file(*d, host.data(), host.data() + sb, state->pos, weights_hash, path);
 }
@@ -723,10 +751,8 @@ gdn_status gdn_state_load(const gdn_desc *d, gdn_state *state, uint64_t weights_
     std::vector<unsigned char> host(sb + cb);
     int64_t pos = 0;
     if ((st = read_state_file(*d, host.data(), host.data() + sb, &pos, weights_hash, path))) return st;
-    hipStream_t hs = (hipStream_t)stream;
-    if (hipMemcpyAsync(state->S, host.data(), sb, hipMemcpyHostToDevice, hs) != hipSuccess ||
-        (cb && hipMemcpyAsync(state->conv, host.data() + sb, cb, hipMemcpyHostToDevice, hs) != hipSuccess) ||
-        hipStreamSynchronize(hs) != hipSuccess)
+    if (copy_to_device(state->S, host.data(), sb, stream) != 0 ||
+        (cb && copy_to_device(state->conv, host.data() + sb, cb, stream) != 0) || stream_sync(stream) != 0)
         return GDN_EDEVICE;
     state->pos = pos;
     state->tag = gdn_desc_tag(d);

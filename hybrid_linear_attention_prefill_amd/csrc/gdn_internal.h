@@ -1,5 +1,10 @@
 // gdn_internal.h -- declarations shared by the host half (gdn_host.cpp) and the kernels
 // (gdn_kernels.hip) of libgdn_prefill.so.  Not part of the public ABI.
+//
+// The host half compiles without ROCm: it reaches the device only through the launch_*
+// functions below, which the HIP sources define.  So the same validation, grid arithmetic,
+// checkpoint ring and state-file code can be built with a plain C++ compiler (and its
+// sanitizers) against a host-memory stand-in for those functions, for CPU tests.
 #pragma once
 #include <cstddef>
 #include <cstdint>
@@ -41,12 +46,14 @@ struct SegArgs {
 };
 
 // Workspace carved for one launch (device pointers).
+// The fp16 arrays are held as raw 16-bit words here (the host half has no fp16 type); the
+// kernels read and write them as _Float16.
 struct Workspace {
-    _Float16 *Qh;  // [n_sub][Hk][64*d]  normalised q, fp16, in MFMA A-fragment order
-    _Float16 *Kh;  // [n_sub][Hk][64*d]  normalised k, likewise: fragment (w, kb) lane l holds
+    uint16_t *Qh;  // [n_sub][Hk][64*d]  normalised q, fp16, in MFMA A-fragment order
+    uint16_t *Kh;  // [n_sub][Hk][64*d]  normalised k, likewise: fragment (w, kb) lane l holds
                    //                    row 16w + l%16, columns 32kb + 8(l/16) .. +7
-    _Float16 *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1 fragments, fp16 (order above)
-    _Float16 *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay fragments, fp16 (order above)
+    uint16_t *Tm;  // [n_sub][Hv][kPackedTri] (I + A)^-1 fragments, fp16 (order above)
+    uint16_t *Mm;  // [n_sub][Hv][kPackedTri] lower(Q K^T) * decay fragments, fp16 (order above)
     float *Fac;    // [n_sub][Hv][4][64]  per row: beta, beta*gamma, gamma, exp(G_n - G) (fp32)
 };
 
@@ -110,5 +117,9 @@ int launch_attention(const AttnArgs &aa, int n_tiles, int Hq, int Hkv, int D, in
                      int out_dtype, void *stream);
 int launch_zero(void *p, size_t bytes, void *stream);
 int launch_copy(void *dst, const void *src, size_t bytes, void *stream);
+// Copies between device memory and host memory on `stream`, and a wait for the stream.
+int copy_to_host(void *host, const void *dev, size_t bytes, void *stream);
+int copy_to_device(void *dev, const void *host, size_t bytes, void *stream);
+int stream_sync(void *stream);
 
 }  // namespace gdn

@@ -317,8 +317,8 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__r
 
     // normalised q, k to the workspace in MFMA A-fragment order (coalesced for the chain)
     {
-        _Float16 *Qg = ws.Qh + ((int64_t)sub * Hk + kh) * kC * D;
-        _Float16 *Kg = ws.Kh + ((int64_t)sub * Hk + kh) * kC * D;
+        _Float16 *Qg = (_Float16 *)ws.Qh + ((int64_t)sub * Hk + kh) * kC * D;
+        _Float16 *Kg = (_Float16 *)ws.Kh + ((int64_t)sub * Hk + kh) * kC * D;
         for (int c = tid; c < kC * D / 8; c += 256) {
             const int f = c / 64, l = c % 64, w = f / (D / 32), kb = f % (D / 32);
             const int off = (16 * w + l % 16) * HS + 32 * kb + 8 * (l / 16);
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__r
                     *(f32x4 *)(AS_OF(hh) + BLK(wave, j) + cc * BROW + 4 * g4) = at;
                 }
             }
-            _Float16 *Mg = ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
+            _Float16 *Mg = (_Float16 *)ws.Mm + ((int64_t)sub * Hv + h) * kPackedTri;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 if (kb == 0 || wave >= 2) {
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__r
                 hv[4 + e] = (_Float16)hi[e];
             }
             const int h = kh * group + hp + hh;
-            *(half8 *)(ws.Tm + ((int64_t)sub * Hv + h) * kPackedTri + (f * 64 + l) * 8) = hv;
+            *(half8 *)((_Float16 *)ws.Tm + ((int64_t)sub * Hv + h) * kPackedTri + (f * 64 + l) * 8) = hv;
         }
         if (hp + 2 < group) __syncthreads();  // A, Tinv and the gates are reused by the next pair
     }
@@ -1394,5 +1394,17 @@ int launch_copy(void *dst, const void *src, size_t bytes, void *stream)
                        (uint32_t *)dst, (const uint32_t *)src, words);
     return (int)hipGetLastError();
 }
+
+int copy_to_host(void *host, const void *dev, size_t bytes, void *stream)
+{
+    return (int)hipMemcpyAsync(host, dev, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream);
+}
+
+int copy_to_device(void *dev, const void *host, size_t bytes, void *stream)
+{
+    return (int)hipMemcpyAsync(dev, host, bytes, hipMemcpyHostToDevice, (hipStream_t)stream);
+}
+
+int stream_sync(void *stream) { return (int)hipStreamSynchronize((hipStream_t)stream); }
 
 }  // namespace gdn

@@ -75,23 +75,28 @@ def gates_from_logits(beta_logit, g_logit, g_scale=1.0):
     return beta, g
 
 
-def layer_inputs(shape, T, seed=0, act_dtype=torch.bfloat16, g_scale=1.0, unit_qk=False):
+def layer_inputs(shape, T, seed=0, act_dtype=torch.bfloat16, g_scale=1.0, unit_qk=False,
+                 v_scale=1.0, beta_shift=0.0):
     """Random layer inputs for T rows.
 
     Returns a dict of CPU tensors: x [T, C] (act dtype), conv_w [C, W] (act dtype, absent
     when W == 0), g, beta [T, Hv] fp32.  ``unit_qk`` scales each q and k head row to unit
     length in float64 before the cast (the one-head fp32 recipe).
+    ``v_scale`` multiplies the v channels (a power of two keeps the cast exact relative to the
+    unscaled draw); ``beta_shift`` is added to the beta logits (a large shift drives beta
+    towards 1).  Both serve stress inputs beyond the stated recipe.
     """
     a = shape.n_k_heads * shape.d_k
     q = rng(seed, STREAM_Q).standard_normal((T, a))
     k = rng(seed, STREAM_K).standard_normal((T, a))
-    v = rng(seed, STREAM_V).standard_normal((T, shape.n_v_heads * shape.d_v))
+    v = rng(seed, STREAM_V).standard_normal((T, shape.n_v_heads * shape.d_v)) * v_scale
     if unit_qk:
         for m in (q, k):
             r = m.reshape(T, shape.n_k_heads, shape.d_k)
             r /= np.sqrt((r * r).sum(-1, keepdims=True))
     x = cast(np.concatenate([q, k, v], axis=1), act_dtype)
-    beta, g = gates_from_logits(rng(seed, STREAM_BETA).standard_normal((T, shape.n_v_heads)),
+    beta, g = gates_from_logits(rng(seed, STREAM_BETA).standard_normal((T, shape.n_v_heads))
+                                + beta_shift,
                                 rng(seed, STREAM_G).standard_normal((T, shape.n_v_heads)),
                                 g_scale)
     out = {"x": x, "g": g, "beta": beta}

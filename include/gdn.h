@@ -177,6 +177,68 @@ gdn_status gdn_state_save(const gdn_desc *desc, const gdn_state *state, uint64_t
 gdn_status gdn_state_load(const gdn_desc *desc, gdn_state *state, uint64_t weights_hash,
                           const char *path, void *stream);
 
+/* ---------------------------------------------------------------- session store */
+
+/* Many sessions over a few device state slots under a byte cap ("The shadow reader", section
+ * "Memory and the disk": resident states are capped; past the cap the least recently used
+ * session goes to disk, one file a session, and comes back exact when it is fed again; without
+ * a disk it is dropped and read again from the start; a planned stop writes every resident
+ * session; a file for other weights or another grid is not read.  "Long context and
+ * sessions", section "Sessions on one engine": a session comes back from a GPU slot, from disk
+ * or fresh, and past the number of GPU slots the least recently used ones leave).
+ *
+ * The caller owns all memory: n_slots device states (S and window buffers) and a table of
+ * max_entries (>= n_slots) entries, one per known session.  At most max_resident =
+ * min(n_slots, cap_bytes / (S bytes + window bytes)) sessions are resident at once.  Files
+ * are <dir>/gdn-<id as 16 hex digits>.state in the state-file format above (written by
+ * gdn_state_save, so a failed write leaves no file).  Host calls; the device work (state
+ * copies, zeroing) runs on `stream` and is synchronised where a file is written or read.
+ * Not thread-safe: one caller at a time per store. */
+enum { GDN_STORE_UNUSED = 0, GDN_STORE_RESIDENT = 1, GDN_STORE_ON_DISK = 2, GDN_STORE_DROPPED = 3 };
+enum { GDN_STORE_WAS_RESIDENT = 0, GDN_STORE_FROM_DISK = 1, GDN_STORE_FRESH = 2 };
+
+typedef struct {
+    uint64_t id;       /* the caller's session id */
+    int64_t pos;       /* the session's position when it last left or entered a slot */
+    uint64_t last_use; /* store clock at its last acquire (least recently used = smallest) */
+    int32_t slot;      /* device slot while resident, else -1 */
+    int32_t where;     /* GDN_STORE_UNUSED / RESIDENT / ON_DISK / DROPPED */
+} gdn_store_entry;
+
+typedef struct {
+    gdn_desc desc;
+    gdn_state *slots;         /* [n_slots] the caller's device states */
+    int32_t n_slots, max_resident;
+    size_t cap_bytes, state_bytes;
+    gdn_store_entry *entries; /* [max_entries] the caller's table */
+    int32_t max_entries, reserved;
+    uint64_t weights_hash, clock;
+    char dir[512];            /* spill directory; "" = no disk (evicted sessions are dropped) */
+} gdn_store;
+
+/* Sets up a store over the caller's slots and entry table; dir may be NULL (no disk).
+ * GDN_EINVAL when the cap holds no state, max_entries < n_slots, a slot lacks a buffer or dir
+ * is too long. */
+gdn_status gdn_store_init(gdn_store *store, const gdn_desc *desc, gdn_state *slots,
+                          int32_t n_slots, size_t cap_bytes, const char *dir,
+                          uint64_t weights_hash, gdn_store_entry *entries, int32_t max_entries);
+/* Makes session `id` resident and most recently used; *state points at its slot, which the
+ * caller then prefills in place (commits move its pos).  *origin: GDN_STORE_WAS_RESIDENT, or
+ * GDN_STORE_FROM_DISK (read back exactly from its file), or GDN_STORE_FRESH (a zero state at
+ * pos 0: a new session, one dropped without a disk, or one whose file was missing, damaged or
+ * made for other weights or grid; the caller reads it again from the start).  When no slot is
+ * free the least recently used resident session is written to its file (or dropped). */
+gdn_status gdn_store_acquire(gdn_store *store, uint64_t id, gdn_state **state, int32_t *origin,
+                             void *stream);
+/* Moves a resident session out of its slot now (to disk, or dropped without one). */
+gdn_status gdn_store_evict(gdn_store *store, uint64_t id, void *stream);
+/* Writes every resident session to its file; they stay resident (a planned stop). */
+gdn_status gdn_store_flush(gdn_store *store, void *stream);
+/* Forgets a session and removes its file. */
+gdn_status gdn_store_drop(gdn_store *store, uint64_t id);
+/* Index of session id in the entry table, or -1. */
+int32_t gdn_store_find(const gdn_store *store, uint64_t id);
+
 /* ---------------------------------------------------------------- compute */
 
 /* Standalone causal depthwise conv over all C channels with the window carried:

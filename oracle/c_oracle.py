@@ -22,21 +22,35 @@ class OracleDesc(ctypes.Structure):
                 ("scale", ctypes.c_double), ("l2_eps", ctypes.c_double)]
 
 
-def build():
-    """Compile liboracle.so from gdn_oracle.c (always recompiles)."""
-    tmp = _LIB + ".tmp%d" % os.getpid()
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+            "-fno-omit-frame-pointer", "-g"]
+
+
+def build(sanitize=False, out=None):
+    """Compile liboracle.so from gdn_oracle.c (always recompiles).  With ``sanitize`` the
+    library is built with AddressSanitizer and UndefinedBehaviorSanitizer (for a process that
+    preloads their runtimes) at ``out``."""
+    out = out or _LIB
+    tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call(["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
-                           "-shared", "-pthread", "-o", tmp, _SRC, "-lm"])
-    os.replace(tmp, _LIB)
+                           "-shared", "-pthread"] + (SANITIZE if sanitize else []) +
+                          ["-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, out)
+    return out
 
 
 def load():
+    """The built library; GDN_ORACLE_LIB names another build of the same source (the
+    sanitizer build of the CPU test run)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("GDN_ORACLE_LIB")
+    if not path:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+    lib = ctypes.CDLL(path)
     P = ctypes.POINTER(ctypes.c_double)
     lib.oracle_gdn_layer.argtypes = [ctypes.POINTER(OracleDesc), ctypes.c_int64, P, P, P, P, P, P,
                                      P, P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,

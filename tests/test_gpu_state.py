@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from hybrid_linear_attention_prefill_amd import synth
-from tests.helpers import TOL, new_state, oracle, rel_l2, run_fork, same_bits, to_dev
+from tests.helpers import assert_parity, new_state, oracle, run_fork, same_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -91,8 +91,7 @@ def test_fork_leaves_state_unchanged_and_matches_oracle(b, desc):
     part["conv_w"] = inp["conv_w"]
     o_ref, S_ref, _ = oracle(desc, part, S0=live.S.cpu().numpy().astype(np.float64),
                              window=synth.f64(live.conv))
-    assert rel_l2(o.float().cpu().numpy(), o_ref) <= TOL
-    assert rel_l2(fork.S.cpu().numpy(), S_ref) <= TOL
+    assert_parity(o, fork.S, o_ref, S_ref, label="fork")
     # and bitwise equal to one FORK over the whole prefix from zero (same 64-row grid)
     o_all, s_all = run_fork(b, desc, dinp, new_state(b, desc), ws=ws)
     torch.cuda.synchronize()
@@ -277,10 +276,8 @@ def test_batched_sequences_equal_single_calls(b, desc):
     sub["conv_w"] = inp["conv_w"]
     o_ref, S_ref, w_ref = oracle(desc, sub, S0=shared.S.double().cpu().numpy(),
                                  window=synth.f64(shared.conv.cpu()))
-    eo = rel_l2(o[cu[k]:cu[k + 1]].float().cpu().numpy(), o_ref)
-    es = rel_l2(outs[k].S.cpu().numpy(), S_ref)
-    print("batched 1024 rows from a shared state: rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
-    assert eo < TOL and es < TOL
+    assert_parity(o[cu[k]:cu[k + 1]], outs[k].S, o_ref, S_ref,
+                  label="batched 1024 rows from a shared state")
     assert np.array_equal(synth.f64(outs[k].conv.cpu()), w_ref)
 
 
@@ -337,3 +334,75 @@ def test_state_file_round_trip_continues_exactly(b, desc, tmp_path):
         b.gdn_state_load(desc, slot, weights + 1, path)
     assert e.value.status == b.GDN_EMISMATCH
     assert same_bits(slot.S, keep) and slot.pos == 1536
+
+
+@pytest.mark.parametrize("cap", [256, 64])
+def test_chained_launches_equal_one_launch(b, desc, monkeypatch, cap):
+    """A sequence longer than the per-launch row cap runs as chained launches, each continuing
+    from the state the previous one wrote; with the cap lowered (GDN_TEST_LAUNCH_ROWS) a
+    1,000-row fork and a 1,536-row commit give the same bits as one launch each."""
+    dinp = to_dev(synth.layer_inputs(SHAPE, 1536, seed=81))
+    ws = b.workspace(desc, 1536)
+    zero = new_state(b, desc)
+    ref_o, ref_s = run_fork(b, desc, dinp, zero, rows=(0, 1000), ws=ws)
+    ref_c = new_state(b, desc)
+    _, ref_co = _commit(b, desc, dinp, ref_c, 0, 1536, ws)
+    torch.cuda.synchronize()
+    monkeypatch.setenv("GDN_TEST_LAUNCH_ROWS", str(cap))
+    o, s = run_fork(b, desc, dinp, zero, rows=(0, 1000), ws=ws)
+    live = new_state(b, desc)
+    n, co = _commit(b, desc, dinp, live, 0, 1536, ws)
+    torch.cuda.synchronize()
+    assert n == 1536 and s.pos == 1000
+    assert same_bits(o, ref_o) and same_bits(s.S, ref_s.S) and same_bits(s.conv, ref_s.conv)
+    assert same_bits(co, ref_co) and same_bits(live.S, ref_c.S) and same_bits(live.conv, ref_c.conv)
+
+
+def test_branches_without_final_states_give_the_same_outputs(b, desc):
+    """gdn_prefill_branches with out=None (scratch final states inside the workspace sized by
+    gdn_workspace_bytes(desc, rows, B)) writes the same o bits as with output states."""
+    lens = [64, 130, 7, 200, 64, 91]
+    total = sum(lens)
+    dinp = to_dev(synth.layer_inputs(SHAPE, total, seed=82))
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    zero = new_state(b, desc)
+    ws = b.workspace(desc, total, len(lens))
+    assert ws.numel() == b.gdn_workspace_bytes(desc, total, len(lens))
+    o1 = torch.empty((total, 32, 128), dtype=torch.bfloat16, device="cuda")
+    o2 = torch.empty_like(o1)
+    outs = [b.State(desc) for _ in lens]
+    b.gdn_prefill_branches(desc, cu, dinp["x"], dinp["conv_w"], dinp["g"], dinp["beta"],
+                           [zero] * len(lens), outs, o1, ws)
+    b.gdn_prefill_branches(desc, cu, dinp["x"], dinp["conv_w"], dinp["g"], dinp["beta"],
+                           [zero] * len(lens), None, o2, ws)
+    torch.cuda.synchronize()
+    assert same_bits(o1, o2)
+
+
+def test_session_store_spill_and_reload_continue_exactly(b, desc, tmp_path):
+    """Two sessions through a store with one resident slot: each acquire of the other session
+    writes the resident one to its file; the reloaded session then continues its commits bit
+    for bit as if it had never left the GPU."""
+    dinp = to_dev(synth.layer_inputs(SHAPE, 2048, seed=83))
+    other = to_dev(synth.layer_inputs(SHAPE, 1024, seed=84))
+    ws = b.workspace(desc, 2048)
+    store = b.SessionStore(desc, 1, b.gdn_state_S_bytes(desc) + b.gdn_state_conv_bytes(desc),
+                           directory=str(tmp_path), weights_hash=0x5EED)
+    a, origin = store.acquire(1)
+    assert origin == b.GDN_STORE_FRESH
+    _commit(b, desc, dinp, a, 0, 1024, ws)
+    o_mid = None
+    s2, origin = store.acquire(2)  # session 1 leaves for its file
+    assert origin == b.GDN_STORE_FRESH and store.entry(1)["where"] == b.GDN_STORE_ON_DISK
+    _commit(b, desc, other, s2, 0, 1024, ws)
+    a, origin = store.acquire(1)  # session 2 leaves; session 1 comes back
+    assert origin == b.GDN_STORE_FROM_DISK and a.pos == 1024
+    n, o_mid = _commit(b, desc, dinp, a, 1024, 2048, ws)
+    torch.cuda.synchronize()
+    ref = new_state(b, desc)
+    _, o_ref = _commit(b, desc, dinp, ref, 0, 2048, ws)
+    torch.cuda.synchronize()
+    assert n == 1024 and a.pos == 2048
+    assert same_bits(o_mid, o_ref[1024:]) and same_bits(a.S, ref.S) and same_bits(a.conv, ref.conv)

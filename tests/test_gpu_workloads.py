@@ -21,7 +21,7 @@ import pytest
 import torch
 
 from hybrid_linear_attention_prefill_amd import synth
-from tests.helpers import TOL, new_state, oracle, rel_l2, run_fork, same_bits
+from tests.helpers import assert_parity, new_state, oracle, run_fork, same_bits
 
 pytestmark = pytest.mark.gpu
 
@@ -71,11 +71,7 @@ def _commit(b, desc, inp, state, ws):
 
 def _check_oracle(desc, host_inp, o_gpu, S_gpu, S0=None, window=None, heads=HEADS):
     o_ref, S_ref, w_ref = oracle(desc, host_inp, S0=S0, window=window, heads=heads)
-    o = o_gpu.float().cpu().numpy()[:, heads]
-    S = S_gpu.cpu().numpy()[heads]
-    eo, es = rel_l2(o, o_ref[:, heads]), rel_l2(S, S_ref[heads])
-    print("rel_l2 o=%.3e S=%.3e" % (eo, es), flush=True)
-    assert eo <= TOL and es <= TOL, (eo, es)
+    assert_parity(o_gpu[:, heads], S_gpu[heads], o_ref[:, heads], S_ref[heads])
     return w_ref
 
 
@@ -246,10 +242,8 @@ def test_32_branches_prefix_sweep(b, desc, P):
             hf = {kk: v[full] for kk, v in host.items() if kk != "conv_w"}
             hf["conv_w"] = host["conv_w"]
             o_ref, S_ref, _ = oracle(desc, hf, heads=HEADS)
-            eo = rel_l2(o[cu[k]:cu[k + 1]].float().cpu().numpy()[:, HEADS],
-                        o_ref[len(full) - nb:, HEADS])
-            es = rel_l2(outs[k].S.cpu().numpy()[HEADS], S_ref[HEADS])
-            assert eo <= TOL and es <= TOL, (k, eo, es)
+            assert_parity(o[cu[k]:cu[k + 1]][:, HEADS], outs[k].S[HEADS],
+                          o_ref[len(full) - nb:, HEADS], S_ref[HEADS], label="branch %d" % k)
 
 
 def test_bf16_output_is_rounded_fp32_output(b):

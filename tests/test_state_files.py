@@ -6,13 +6,14 @@ made for other layers reads as missing, and a failed write leaves the slot missi
 stale ("Long context and sessions", section "On disk, across reloads").  Everything here runs
 through the library's host-buffer forms; no device memory is touched.
 """
+import ctypes
 import os
 import struct
 
 import numpy as np
 import pytest
 
-from hybrid_linear_attention_prefill_amd import binding as b
+from tests import hostlib as b
 
 WEIGHTS = 0x5EED5EED12345678
 
@@ -68,7 +69,7 @@ def test_other_layer_grid_dtype_or_weights_is_refused(tmp_path):
     assert _read_status(small_desc(grid=2048), path) == b.GDN_EMISMATCH
     assert _read_status(b.make_desc(2, 4, 128, 128), path) == b.GDN_EMISMATCH
     assert _read_status(b.make_desc(1, 4, 64, 64), path) == b.GDN_EMISMATCH
-    assert _read_status(small_desc(act_dtype=b.torch.float32), path) == b.GDN_EMISMATCH
+    assert _read_status(small_desc(act_dtype="float32"), path) == b.GDN_EMISMATCH
     assert _read_status(d, path, weights=WEIGHTS + 1) == b.GDN_EMISMATCH
     # scale and eps do not change what a state means: the same file reads
     assert _read_status(small_desc(scale=0.3, l2_eps=1e-3), path) == b.GDN_OK
@@ -81,9 +82,9 @@ def test_refused_read_leaves_the_buffers(tmp_path):
     b.gdn_state_file_write(d, S, conv, 512, WEIGHTS, path)
     dst_S = np.full_like(S, 7.0)
     dst_c = np.full_like(conv, 9)
-    pos = b.ctypes.c_int64(-3)
-    st = b.lib.gdn_state_file_read(b.ctypes.byref(d), dst_S.ctypes.data, dst_c.ctypes.data,
-                                   b.ctypes.byref(pos), WEIGHTS + 5, os.fsencode(path))
+    pos = ctypes.c_int64(-3)
+    st = b.lib.gdn_state_file_read(ctypes.byref(d), dst_S.ctypes.data, dst_c.ctypes.data,
+                                   ctypes.byref(pos), WEIGHTS + 5, os.fsencode(path))
     assert st == b.GDN_EMISMATCH
     assert (dst_S == 7.0).all() and (dst_c == 9).all() and pos.value == -3
 
@@ -146,7 +147,7 @@ def test_rewrite_replaces_the_session(tmp_path):
 
 
 def test_no_conv_layer_and_argument_checks(tmp_path):
-    d = b.make_desc(1, 1, 64, 64, conv_width=0, act_dtype=b.torch.float32)
+    d = b.make_desc(1, 1, 64, 64, conv_width=0, act_dtype="float32")
     S = np.arange(64 * 64, dtype=np.float32).reshape(1, 64, 64)
     path = str(tmp_path / "one.gdn")
     b.gdn_state_file_write(d, S, None, 0, 0, path)
@@ -156,7 +157,7 @@ def test_no_conv_layer_and_argument_checks(tmp_path):
     with pytest.raises(b.GdnError) as e:
         b.gdn_state_file_write(d, S, None, -1, 0, path)
     assert e.value.status == b.GDN_EINVAL
-    assert b.lib.gdn_state_file_write(b.ctypes.byref(d), S.ctypes.data, None, 0, 0, None) == b.GDN_EINVAL
+    assert b.lib.gdn_state_file_write(ctypes.byref(d), S.ctypes.data, None, 0, 0, None) == b.GDN_EINVAL
     d4 = small_desc()
-    assert b.lib.gdn_state_file_write(b.ctypes.byref(d4), S.ctypes.data, None, 0, 0,
+    assert b.lib.gdn_state_file_write(ctypes.byref(d4), S.ctypes.data, None, 0, 0,
                                       os.fsencode(path)) == b.GDN_EINVAL  # window required
