@@ -12,15 +12,17 @@ TOL = 2e-3  # relative L2 bound on outputs and final state against the float64 o
 #  - o, per (row t, value head h): ||e_t|| <= ROW_REL ||ref_t|| + ROW_ABS RMS_h.  ROW_REL is
 #    2^-9, the largest relative change round-to-nearest-even to bf16 makes to any vector (it
 #    covers the bf16 rounding of o); ROW_ABS covers the fp16 operand rounding upstream, which
-#    does not scale with a row's own norm (a row can be small by cancellation).  Measured on
-#    the 16/32/128 layer at 8,192 rows, slow decay with beta near 1, and |v| scaled by 2^-12
-#    .. 2^13: the smallest ROW_ABS that passes was 0.7e-3 .. 1.8e-3.
+#    does not scale with a row's own norm (a row can be small by cancellation, e.g. a small
+#    q.k of the first row).  Measured on the 16/32/128 layer at 8,192 rows, slow decay with
+#    beta near 1, and |v| scaled by 2^-12 .. 2^13: the smallest ROW_ABS that passes was
+#    0.7e-3 .. 1.8e-3; a one-row call needed 3.1e-3.  In a call shorter than one sub-chunk a
+#    head has too few rows for a stable RMS, so RMS_h there is pooled over all heads.
 #  - o with fp32 output, per element: |e| <= ELEM_REL |ref| + ELEM_ABS rms_h (rms_h over the
 #    head's elements); measured need 3.2e-3 .. 8.4e-3 for ELEM_ABS at ELEM_REL = 4e-3.
 #  - S, per value head: relative L2 <= TOL; per (head, d_k row): ||e|| <= S_ROW RMS_h
 #    (measured at most 2.9e-3).
 ROW_REL = 2.0 ** -9
-ROW_ABS = 3e-3
+ROW_ABS = 4e-3
 ELEM_REL, ELEM_ABS = 4e-3, 1.5e-2
 S_ROW = 5e-3
 
@@ -45,7 +47,10 @@ def assert_parity(o_gpu, S_gpu, o_ref, S_ref, heads=None, tol=TOL, label=""):
     e = o - o_ref
     rn = np.linalg.norm(e, axis=-1)                                  # [T, H]
     rr = np.linalg.norm(o_ref, axis=-1)
-    rms = np.sqrt((rr ** 2).mean(axis=0)) if o.shape[0] else np.ones(o.shape[1])
+    if o.shape[0] >= 64:
+        rms = np.sqrt((rr ** 2).mean(axis=0))
+    else:  # pooled over heads (too few rows per head)
+        rms = np.full(o.shape[1], np.sqrt((rr ** 2).mean()) if o.size else 1.0)
     row_q = (rn - ROW_REL * rr) / np.maximum(rms[None, :], 1e-300)  # needed ROW_ABS per row
     es_h = np.linalg.norm((S - S_ref).reshape(S.shape[0], -1), axis=1) / np.maximum(
         np.linalg.norm(S_ref.reshape(S.shape[0], -1), axis=1), 1e-300)
