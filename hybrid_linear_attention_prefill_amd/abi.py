@@ -114,6 +114,8 @@ def signatures():
         "gdn_prefill_chunked_events": (I32, [D, V, V, V, V, S, S, V, I64, I32,
                                              ctypes.POINTER(ctypes.c_int64), V, SZ, V,
                                              ctypes.POINTER(ctypes.c_void_p), I32]),
+        "gdn_prefill_chunked_noalloc": (I32, [D, V, V, V, V, S, S, V, I64, I32,
+                                              ctypes.POINTER(ctypes.c_int64), V]),
         "gdn_prefill_branches": (I32, [D, I32, ctypes.POINTER(ctypes.c_int64), V, V, V, V,
                                        ctypes.POINTER(S), ctypes.POINTER(S), V, V, SZ, V]),
         "gdn_decode_step": (I32, [D, I32, V, V, V, V, ctypes.POINTER(S), ctypes.POINTER(S), V, V]),
@@ -144,9 +146,17 @@ def signatures():
     }
 
 
-def declare(lib):
-    """Sets restype and argtypes of every declared function on a loaded library."""
+# Functions defined in the HIP sources only (absent from a host-only build of the host half).
+DEVICE_ONLY = ("gdn_prefill_chunked_noalloc",)
+NOALLOC_WORKSPACE_BYTES = 32 << 20
+
+
+def declare(lib, host_only=False):
+    """Sets restype and argtypes of every declared function on a loaded library (with
+    host_only, of those a host-only build defines)."""
     for name, (res, args) in signatures().items():
+        if host_only and name in DEVICE_ONLY:
+            continue
         f = getattr(lib, name)
         f.restype, f.argtypes = res, args
     return lib

@@ -155,6 +155,19 @@ def gdn_prefill_chunked(desc, x, conv_w, g, beta, state_in, state_out, o, T=None
     return rows.value
 
 
+def gdn_prefill_chunked_noalloc(desc, x, conv_w, g, beta, state_in, state_out, o, T=None,
+                                mode=GDN_COMMIT, stream=None):
+    """gdn_prefill_chunked with the library's static workspace (no workspace argument).
+    Returns rows_done."""
+    T = x.shape[0] if T is None else T
+    rows = ctypes.c_int64(-1)
+    st = lib.gdn_prefill_chunked_noalloc(ctypes.byref(desc), _ptr(x), _ptr(conv_w), _ptr(g),
+                                         _ptr(beta), state_in.ref(), state_out.ref(), _ptr(o),
+                                         int(T), int(mode), ctypes.byref(rows), _stream(stream))
+    _check(st, "gdn_prefill_chunked_noalloc")
+    return rows.value
+
+
 def gdn_prefill_chunked_events(desc, x, conv_w, g, beta, state_in, state_out, o, T=None,
                                mode=GDN_COMMIT, ws=None, events=(), stream=None):
     """gdn_prefill_chunked recording torch.cuda.Event objects around each kernel."""

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libgdn_prefill.so")
 SOURCES = [os.path.join(PKG, "csrc", "gdn_host.cpp"), os.path.join(PKG, "csrc", "gdn_store.cpp"),
            os.path.join(PKG, "csrc", "gdn_kernels.hip"),
-           os.path.join(PKG, "csrc", "gdn_linear.hip"), os.path.join(PKG, "csrc", "gdn_attention.hip")]
+           os.path.join(PKG, "csrc", "gdn_linear.hip"), os.path.join(PKG, "csrc", "gdn_attention.hip"),
+           os.path.join(PKG, "csrc", "gdn_noalloc.hip")]
 ARCH = "gfx950"
 
 # Packed fp32 arithmetic is switched off for all device code.

@@ -281,6 +281,23 @@ gdn_status gdn_prefill_chunked_events(const gdn_desc *desc, const void *x, const
                                       int64_t *rows_done, void *ws, size_t ws_bytes,
                                       void *stream, void *const *events, int32_t n_events);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): gdn_prefill_chunked with the workspace in a static
+ * device array of GDN_NOALLOC_WORKSPACE_BYTES that the library holds on every GPU it runs on
+ * until the process ends (32 MiB: about 2,200 rows of a 16/32/128 layer, enough for a pending
+ * tail plus a question).  Arguments, results and refusals are gdn_prefill_chunked's; a call
+ * whose rows need more workspace than the array (gdn_workspace_bytes(desc, rows, 1) >
+ * GDN_NOALLOC_WORKSPACE_BYTES) is refused with GDN_EWORKSPACE and enqueues nothing.  The
+ * library allocates nothing here; `stream` must belong to the current device.  Every call on
+ * one GPU uses the same array: calls that overlap in time on one GPU (other streams or
+ * threads) race, so a caller serialises them.  GDN_EDEVICE if the array's address cannot be
+ * had. */
+#define GDN_NOALLOC_WORKSPACE_BYTES (32u << 20)
+gdn_status gdn_prefill_chunked_noalloc(const gdn_desc *desc, const void *x, const void *conv_w,
+                                       const float *g, const float *beta, const gdn_state *in,
+                                       gdn_state *out, void *o, int64_t T, int32_t mode,
+                                       int64_t *rows_done, void *stream);
+
 /* Batched branch continuation: B sequences packed along rows.  Branch b owns rows
  * [cu_rows[b], cu_rows[b+1]) of x, g, beta and o (cu_rows is a host array of B+1
  * non-decreasing offsets starting at 0; every branch has >= 1 row) and starts from

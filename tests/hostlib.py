@@ -27,7 +27,7 @@ if not _path:
     _path = build_hostcheck.lib_path()
     if build_hostcheck.stale(_path):
         build_hostcheck.build()
-lib = abi.declare(ctypes.CDLL(_path))
+lib = abi.declare(ctypes.CDLL(_path), host_only=True)
 lib.gdn_hostcheck_launches.restype = ctypes.c_int32
 lib.gdn_hostcheck_launches.argtypes = []
 lib.gdn_hostcheck_reset.restype = None

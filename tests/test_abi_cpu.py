@@ -36,7 +36,8 @@ def test_hip_library_loads_and_exports_every_declared_symbol():
                | set(re.findall(r"^class (\w+)", src, re.M)))
     for n in names:
         assert hasattr(hip, n), n
-        assert hasattr(b.lib, n), n  # the host-only build exports the same host half
+        if n not in abi.DEVICE_ONLY:
+            assert hasattr(b.lib, n), n  # the host-only build exports the same host half
         # the checkpoint ring and the session store are wrapped as classes (CkptRing, SessionStore)
         as_method = n.startswith("gdn_ckpt_") or n.startswith("gdn_store_")
         assert n in wrapped or as_method, "binding lacks " + n
