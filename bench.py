@@ -6,17 +6,24 @@ Workload: one GDN layer with 16 key heads and 32 value heads of width 128, bf16 
 fp32 state, width-4 causal conv with state, commit grid 512, sub-chunks of 64 rows; one step
 commits T = 8192 rows (conv, L2 norm, gates, WY/UT factors, the state chain, outputs and the
 new conv window).  Inputs are seeded synthetic tensors resident in HBM before timing starts;
-three input sets rotate so that consecutive steps do not re-read the previous step's inputs
-from the 256 MB Infinity Cache.
+three input sets rotate.
 
-Prints one JSON line with the whole-job tokens/s (wall clock over the timed steps), a
-roofline object for the dominant kernel (its share of the layer's algorithmic bytes over its
-average duration, from HIP events the library records on the launch stream around each
-kernel in every timed step), the same figure for the whole layer call, and the float64 CPU
-oracle timed on a bounded sample of the same workload.
+Timing protocol (cold cache): before each timed call a 512 MiB scratch buffer is read, which
+evicts the 256 MB Infinity Cache and leaves it holding clean lines (a write would leave 256 MB
+of dirty lines that the timed call then pays to write back); HIP events on the launch stream bracket the call and, recorded
+by the library, each of its kernels.  `value` is T over the median call duration of the K timed
+steps (`ms_per_step` is that median).  The same K calls back to back without the flush give the
+warm rate, labelled as such.
+
+Prints one JSON line with those rates, a roofline object for the dominant kernel (its share of
+the layer's algorithmic bytes over its average duration in the timed steps) and for the whole
+call, the other workloads (the one-head fp32 layer; the multi-turn replay with forks; the
+24-layer long session with checkpoints and a divergence; 32 batched branches against one
+prefill per branch), and the float64 CPU oracle timed on bounded samples.
 
     --extras                also time state capture/restore, a 370-row fork, decode steps
                             of 1 and 32 sessions, the two projections and the attention layer
+    --no-workloads          skip the one-head and session workloads
     --copy-calibration N    run a plain N-byte device copy after timing (for counter scaling)
 """
 import argparse
@@ -84,12 +91,21 @@ def algorithmic_flops(T, Hk, Hv, d, C=64):
 
 
 def cpu_baseline(seconds_target=10.0):
-    """The float64 oracle on a bounded sample of the workload: whole 8192-row layer calls (all
-    32 value heads, threads over heads), repeated until about `seconds_target` of wall time."""
+    """The float64 oracle on bounded samples of the workloads: whole 8192-row calls of the
+    16/32/128 layer (all 32 value heads, threads over heads) until about `seconds_target` of
+    wall time; the same layer on one thread (1,024 rows); and the one-head fp32 layer (1,024
+    rows, no conv).  The session workloads run the 16/32/128 layer shape, so their per-row
+    oracle cost is the layer's."""
     import numpy as np
     from hybrid_linear_attention_prefill_amd import synth
     from oracle import c_oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    nproc = os.cpu_count() or 1
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = nproc
+    # the box's CPU share for one GPU is 16 threads; the layer has 32 independent chains
+    threads = max(1, min(16, avail, 32))
     shape = synth.LAYER_16x32x128
     kw = dict(n_k_heads=16, n_v_heads=32, d_k=128, d_v=128, scale=128 ** -0.5, l2_eps=1e-6)
     inp = synth.layer_inputs(shape, T_ROWS, seed=0)
@@ -102,10 +118,29 @@ def cpu_baseline(seconds_target=10.0):
                            np.zeros((32, 128, 128)), threads=threads, **kw)
         spent += time.perf_counter() - t0
         calls += 1
+    n1 = 1024
+    t0 = time.perf_counter()
+    c_oracle.gdn_layer(x[:n1], w, np.zeros((3, shape.channels)), g[:n1], beta[:n1],
+                       np.zeros((32, 128, 128)), threads=1, **kw)
+    one = n1 / (time.perf_counter() - t0)
+    c1 = synth.layer_inputs(synth.ONE_HEAD, 1024, seed=0, act_dtype=__import__("torch").float32,
+                            unit_qk=True)
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 1.0:
+        c_oracle.gdn_layer(synth.f64(c1["x"]), None, None, synth.f64(c1["g"]), synth.f64(c1["beta"]),
+                           np.zeros((1, 64, 64)), n_k_heads=1, n_v_heads=1, d_k=64, d_v=64,
+                           scale=64 ** -0.5, l2_eps=1e-6, threads=1)
+        reps += 1
+    c1_rate = reps * 1024 / (time.perf_counter() - t0)
     return {"value": calls * T_ROWS / spent, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "nproc": nproc, "cpus_available": avail,
+            "one_thread_tokens_per_s": round(one, 1),
+            "one_head_fp32_tokens_per_s": round(c1_rate, 1),
             "sample": "float64 per-token oracle (conv, L2 norm, gated delta rule) on the same "
-                      "16/32/128 layer: %d whole 8192-row calls, %.1f s wall" % (calls, spent)}
+                      "16/32/128 layer: %d whole 8192-row calls, %.1f s wall, %d threads over "
+                      "heads; one thread on 1,024 rows; the one-head fp32 layer of 1,024 rows on "
+                      "one thread" % (calls, spent, threads)}
 
 
 def session_workloads(b, synth, desc, dev, shape):
@@ -296,6 +331,33 @@ def session_workloads(b, synth, desc, dev, shape):
     return res
 
 
+def one_head_rate(b, synth, dev, reps=50):
+    """The one-head fp32 layer (d = 64, T = 1,024, inputs post-conv, FORK from zero): tokens/s
+    from the median of per-call HIP events.  Latency-bound (16 sub-chunks of one chain)."""
+    import torch
+    d1 = b.make_desc(1, 1, 64, 64, conv_width=0, act_dtype=torch.float32, out_dtype=torch.float32)
+    inp = {k: v.to(dev) for k, v in synth.layer_inputs(synth.ONE_HEAD, 1024, seed=0,
+                                                       act_dtype=torch.float32, unit_qk=True).items()}
+    z, out = b.State(d1), b.State(d1)
+    b.gdn_state_init(d1, z)
+    o = torch.empty((1024, 1, 64), dtype=torch.float32, device=dev)
+    ws = b.workspace(d1, 1024)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for _ in range(3):
+        b.gdn_prefill_chunked(d1, inp["x"], None, inp["g"], inp["beta"], z, out, o, 1024, b.GDN_FORK, ws)
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        e0.record(stream)
+        b.gdn_prefill_chunked(d1, inp["x"], None, inp["g"], inp["beta"], z, out, o, 1024, b.GDN_FORK, ws)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)[reps // 2]
+    return {"T": 1024, "d": 64, "heads": 1, "dtype": "fp32", "us_median": round(ms * 1e3, 2),
+            "tokens_per_s": round(1024 / (ms * 1e-3), 1)}
+
+
 def measured_peaks(dev):
     """Reference rates measured on the box: a 1 GiB device-to-device copy (HBM read + write),
     and torch's bf16 matmul (the vendor BLAS) at the layer's two projection shapes, beside
@@ -379,9 +441,9 @@ def main():
     ap.add_argument("--peaks", action="store_true",
                     help="also measure a device copy and torch's bf16 matmul at the projection "
                          "shapes, as reference rates")
-    ap.add_argument("--workloads", action="store_true",
-                    help="also time the session workloads (multi-turn replay with forks, the "
-                         "24-layer long session, 32 batched branches)")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the one-head layer and the session workloads (multi-turn replay "
+                         "with forks, the 24-layer long session, 32 batched branches)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed region, run a plain device copy of BYTES bytes three "
                          "times (reference dispatch for the HBM byte counters)")
@@ -421,33 +483,43 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-
-    # Timed region 1: K layer calls back to back (the throughput figure).
     stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1) / args.steps
 
-    # Timed region 2: the same K calls with HIP events recorded by the library on the launch
-    # stream around each of its three kernels (the per-kernel durations).
-    # (the library's third event pair brackets no kernel: the chain kernel writes the window)
+    # Timed region: K steps, each a read of a 512 MiB scratch buffer (evicting the 256 MB
+    # Infinity Cache, which then holds clean lines) and then one layer call; HIP events recorded by the library on the launch
+    # stream bracket each of its kernels (pair 0 the prep kernel, pair 1 the chain kernel; pair
+    # 2 brackets no kernel), so the call runs from event 0 to event 3 and excludes the flush.
+    scratch = torch.ones((512 << 20) // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty((), dtype=torch.int64, device=dev)
     names = ("prep_kernel", "chain_kernel")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     for e in [e for row in evs for e in row]:
         e.record(stream)              # creates the underlying HIP events before timing
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for i in range(args.steps):
+        torch.sum(scratch, 0, dtype=torch.int64, out=sink)
         step(i, evs[i])
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sorted(row[0].elapsed_time(row[3]) for row in evs)
+    med_ms = call_ms[len(call_ms) // 2] if len(call_ms) % 2 else \
+        0.5 * (call_ms[len(call_ms) // 2 - 1] + call_ms[len(call_ms) // 2])
     per_kernel = {n: sum(row[2 * k].elapsed_time(row[2 * k + 1]) for row in evs) / args.steps
                   for k, n in enumerate(names)}
+    del scratch, sink
+
+    # Warm: the same K calls back to back (inputs and workspace partly in the Infinity Cache).
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    warm_wall = time.perf_counter() - tw
+    warm_ms = ev0.elapsed_time(ev1) / args.steps
 
     extras = {}
     if args.extras:
@@ -555,8 +627,10 @@ def main():
                                        "mfma_bf16_frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4)}
         del aq, ak, av, ao
 
-    if args.workloads:
-        extras["workloads"] = session_workloads(b, synth, desc, dev, shape)
+    workloads = None
+    if not args.no_workloads:
+        workloads = {"one_head_fp32_T1024": one_head_rate(b, synth, dev)}
+        workloads.update(session_workloads(b, synth, desc, dev, shape))
     if args.peaks:
         extras["measured_peaks"] = measured_peaks(dev)
 
@@ -573,10 +647,11 @@ def main():
     per_token, bytes_call = algorithmic_bytes(T_ROWS, Hk, Hv, d)
     split = kernel_bytes(T_ROWS, Hk, Hv, d)
     flops_call = algorithmic_flops(T_ROWS, Hk, Hv, d)
-    tokens_per_s = T_ROWS * args.steps / wall
+    tokens_per_s = T_ROWS / (med_ms * 1e-3)
     dom = max(per_kernel, key=per_kernel.get)
     dom_achieved = split[dom] / (per_kernel[dom] * 1e-3) / 1e9
-    layer_achieved = bytes_call / (ev_ms * 1e-3) / 1e9
+    layer_achieved = bytes_call / (med_ms * 1e-3) / 1e9
+    ev_ms = med_ms
     out = {
         "metric": "Gated-DeltaNet prefill tokens/sec per layer (1 MI355X); % of MFMA/HBM roofline",
         "value": round(tokens_per_s, 1),
@@ -584,7 +659,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "ms_per_step": round(med_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -593,6 +668,17 @@ def main():
         "config": {"workload": "gdn_layer_commit_prefill", "T": T_ROWS, "n_k_heads": Hk,
                    "n_v_heads": Hv, "d_k": d, "d_v": d, "conv_width": 4, "grid": 512,
                    "sub_chunk": 64, "act_dtype": "bf16", "out_dtype": "bf16"},
+        "timing": {
+            "protocol": "cold cache: a 512 MiB scratch read before each timed call; value and "
+                        "ms_per_step from the median of the per-call HIP event durations",
+            "call_ms_median": round(med_ms, 5), "call_ms_min": round(call_ms[0], 5),
+            "call_ms_max": round(call_ms[-1], 5),
+            "call_ms_mean": round(sum(call_ms) / len(call_ms), 5),
+            "timed_region_wall_s": round(wall, 4),
+            "warm_back_to_back": {"tokens_per_s": round(T_ROWS * args.steps / warm_wall, 1),
+                                  "ms_per_call_events": round(warm_ms, 5),
+                                  "label": "warm: the K calls back to back, no flush"},
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": dom,
@@ -617,6 +703,8 @@ def main():
             },
         },
     }
+    if workloads:
+        out["workloads"] = workloads
     if extras:
         out["extras"] = extras
     if not args.no_cpu_baseline:
