@@ -29,8 +29,20 @@
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and the call
  *    returns without synchronising.  GDN_EDEVICE reports a failed launch or copy; the
  *    outputs are then undefined.
- *  - The library holds no global mutable state; calls on different streams may overlap as
- *    long as they write disjoint memory (and use different workspaces).
+ *  - The library holds no global mutable state (gdn_prefill_chunked_noalloc's static
+ *    workspace aside); calls on different streams may overlap as long as they write disjoint
+ *    memory (and use different workspaces).  GDN_TEST_LAUNCH_ROWS in the environment (a
+ *    positive multiple of 64) lowers the rows a prefill launch takes, for tests of the
+ *    chained-launch path; it never raises them.
+ *  - Admissible magnitudes.  The prefill's matrix products take fp16 operands (11-bit
+ *    significand, range 6.1e-5 .. 65504) with fp32 accumulation: the normalised q and k, the
+ *    factors Tinv and M (|entries| <= 1 in practice), and, scaled with the values, an fp16 copy
+ *    of the state S, R = beta v - beta gamma K S and D = Tinv R.  Outputs and states match the
+ *    float64 per-token rule to 2e-3 relative L2 while the largest |S| entry and the largest
+ *    post-conv |v| of a call stay within about 1e-4 .. 2e4 (measured on the 16/32/128 layer:
+ *    max |S| from 1.3e-4 to 2.4e4 passes; at 8e-6, fp16 subnormals give 9e-3; at 4.7e4 an fp16
+ *    operand overflows and the outputs are not finite).  The state itself, the gates, conv and
+ *    norms are fp32 throughout.
  *
  * Layouts (row-major, innermost last):
  *   C   = 2*n_k_heads*d_k + n_v_heads*d_v conv channels, ordered q | k | v, each head's
@@ -116,26 +128,39 @@ size_t gdn_state_S_bytes(const gdn_desc *desc);
 size_t gdn_state_conv_bytes(const gdn_desc *desc);
 
 /* Device workspace needed by a prefill call of at most max_rows rows in total over at most
- * max_segments sequences (1 for gdn_prefill_chunked, B for gdn_prefill_branches).
+ * max_segments sequences (1 for gdn_prefill_chunked, B for gdn_prefill_branches; with B it also
+ * covers the scratch final states of a branch batch given no output states).
  * 0 on an invalid descriptor. */
 size_t gdn_workspace_bytes(const gdn_desc *desc, int64_t max_rows, int32_t max_segments);
 
 /* ---------------------------------------------------------------- state operations */
 
-/* Zero S and the window on `stream`; pos = 0; tag = gdn_desc_tag(desc). */
+/* Zero S and the window on `stream`; pos = 0; tag = gdn_desc_tag(desc).  The state a session
+ * starts from, and the one a restore falls back to when no checkpoint lies at or below the
+ * first differing token ("The shadow reader", section "Exact on a grid").  Refuses a
+ * destination whose S is not 4-byte or whose window is not 16-byte aligned (GDN_EINVAL). */
 gdn_status gdn_state_init(const gdn_desc *desc, gdn_state *state, void *stream);
 
-/* snap <- live: device copies of S and the window plus pos and tag.  Refuses a live state
- * of another tag (GDN_EMISMATCH) and snap == live or overlapping buffers (GDN_EALIAS). */
+/* snap <- live: device copies of S and the window plus pos and tag ("Long context and
+ * sessions", section "Sessions on one engine": a session's state is saved into a slot as a GPU
+ * copy; "The shadow reader", section "One session's state": a checkpoint of the recurrent state
+ * at a turn's end).  Refuses a live state of another tag (GDN_EMISMATCH), snap == live or
+ * overlapping buffers (GDN_EALIAS) and a misaligned snap (GDN_EINVAL). */
 gdn_status gdn_state_capture(const gdn_desc *desc, const gdn_state *live, gdn_state *snap,
                              void *stream);
 
-/* live <- snap.  Refuses a snapshot whose tag is not the descriptor's (GDN_EMISMATCH):
- * a state for another layer shape or grid is not read. */
+/* live <- snap ("Long context and sessions", section "Sessions on one engine": a slot is loaded
+ * back exactly, and a state made for other layers is refused; "The shadow reader", section
+ * "Exact on a grid": on a differing prompt the newest checkpoint at or below the first
+ * differing token is restored).  Refuses a snapshot whose tag is not the descriptor's
+ * (GDN_EMISMATCH): a state for another layer shape or grid is not read. */
 gdn_status gdn_state_restore(const gdn_desc *desc, gdn_state *live, const gdn_state *snap,
                              void *stream);
 
-/* dst[i] <- src for i in [0, n): n device copies (slots for a batch of branches). */
+/* dst[i] <- src for i in [0, n): n device copies (slots for a batch of branches, or the scratch
+ * state a question runs in while the committed state stays as it was: "The shadow reader",
+ * section "Exact on a grid"; PR "qwen3_5: run prompts that share prefixes once per prefix",
+ * section Purpose: every branch continues from a copy of the shared prefix state). */
 gdn_status gdn_state_fork(const gdn_desc *desc, const gdn_state *src, gdn_state *dst, int32_t n,
                           void *stream);
 
@@ -241,7 +266,9 @@ int32_t gdn_store_find(const gdn_store *store, uint64_t id);
 
 /* ---------------------------------------------------------------- compute */
 
-/* Standalone causal depthwise conv over all C channels with the window carried:
+/* Standalone causal depthwise conv over all C channels with the window carried (PR "qwen3_5:
+ * run prompts that share prefixes once per prefix", section Purpose: the state of a linear-
+ * attention layer holds the three most recent conv inputs, which a continuation needs):
  * xt = window ++ x; y[t][c] = sum_j conv_w[c][j] * xt[t+j][c] (SiLU if desc->conv_silu);
  * the window becomes the last W-1 rows of xt.  y [T][C] in desc->out_dtype (device),
  * x [T][C] act dtype (device), window [W-1][C] act dtype (device, updated in place).
@@ -250,7 +277,11 @@ int32_t gdn_store_find(const gdn_store *store, uint64_t id);
 gdn_status conv1d_state_step(const gdn_desc *desc, const void *x, const void *conv_w, void *window,
                              void *y, int64_t T, void *stream);
 
-/* Prefill T rows of one sequence from state `in` into state `out`, writing o.
+/* Prefill T rows of one sequence from state `in` into state `out`, writing o ("The shadow
+ * reader", section "Exact on a grid": the state advances in whole grid chunks at absolute
+ * positions; the rows past the last grid line wait as the pending tail; a question runs the
+ * tail plus its own rows from the committed state in a fork that leaves that state as it was;
+ * a replay equals a fresh prefill bit for bit).
  *
  * GDN_COMMIT: requires in->pos % grid == 0.  Absorbs rows_done = floor(T / grid) * grid
  *   rows (the rest is the caller's pending tail) and writes o rows [0, rows_done).
@@ -298,7 +329,11 @@ gdn_status gdn_prefill_chunked_noalloc(const gdn_desc *desc, const void *x, cons
                                        gdn_state *out, void *o, int64_t T, int32_t mode,
                                        int64_t *rows_done, void *stream);
 
-/* Batched branch continuation: B sequences packed along rows.  Branch b owns rows
+/* Batched branch continuation (PR "qwen3_5: run prompts that share prefixes once per prefix",
+ * section Purpose: each prefix runs once up to its last multiple of 64 rows, and every branch
+ * continues from the shared fp32 state and conv window with the remainder at its head; section
+ * "Test Plan": branches equal plain passes over their full prompts): B sequences packed along
+ * rows.  Branch b owns rows
  * [cu_rows[b], cu_rows[b+1]) of x, g, beta and o (cu_rows is a host array of B+1
  * non-decreasing offsets starting at 0; every branch has >= 1 row) and starts from
  * init[b], whose pos must be a multiple of 64.  init entries may repeat (a shared prefix
