@@ -81,6 +81,21 @@ def measured_traffic(kernel):
     return None if v is None else int(float(v))
 
 
+def warm_clock(call, seconds=0.25):
+    """Repeat `call` for about `seconds` of wall time (untimed), so that a compute-bound kernel
+    is timed at the clock it settles to under load rather than while the clock is still
+    ramping up from the lighter work before it."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        call()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def algorithmic_flops(T, Hk, Hv, d, C=64):
     """Flops of the chunked method per call: K K^T and Q K^T per key head (lower triangle),
     and per value head the products with the state, the triangular T R and M D, and the
@@ -585,9 +600,8 @@ def main():
             px = torch.randn((T_ROWS, K), device=dev).to(torch.bfloat16)
             pw = (torch.randn((N, K), device=dev) / K ** 0.5).to(torch.bfloat16)
             py = torch.empty((T_ROWS, N), dtype=torch.bfloat16, device=dev)
-            for _ in range(3):
-                b.gdn_linear(px, pw, py)
-            reps4 = 20
+            warm_clock(lambda: b.gdn_linear(px, pw, py))
+            reps4 = 50
             e2.record(stream)
             for _ in range(reps4):
                 b.gdn_linear(px, pw, py)
@@ -610,9 +624,8 @@ def main():
         av = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
         ao = torch.empty_like(aq)
         adesc = b.make_attn_desc(Hq_a, Hkv_a, D_a)
-        for _ in range(2):
-            b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)])
-        reps5 = 10
+        warm_clock(lambda: b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)]))
+        reps5 = 20
         e2.record(stream)
         for _ in range(reps5):
             b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)])
