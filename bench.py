@@ -615,6 +615,26 @@ def main():
                 "hbm_frac": round(gbps / HBM_PEAK_GBS, 4)}
             del ping, pong
 
+        # the standalone conv with its window over the layer's channels (bf16 in and out)
+        cx = sets[0]["x"]
+        cwin = torch.zeros((3, cx.shape[1]), dtype=torch.bfloat16, device=dev)
+        cy = torch.empty_like(cx)
+        warm_clock(lambda: b.conv1d_state_step(desc, cx, sets[0]["conv_w"], cwin, cy), 0.1)
+        reps6 = 20
+        e2.record(stream)
+        for _ in range(reps6):
+            b.conv1d_state_step(desc, cx, sets[0]["conv_w"], cwin, cy)
+        e3.record(stream)
+        torch.cuda.synchronize()
+        conv_ms = e2.elapsed_time(e3) / reps6
+        conv_bytes = 2 * cx.numel() * 2 + 4 * cx.shape[1] * 2 + 2 * 3 * cx.shape[1] * 2
+        extras["conv1d_state_step"] = {"T": T_ROWS, "channels": int(cx.shape[1]),
+                                       "us": round(conv_ms * 1e3, 2),
+                                       "algorithmic_bytes": conv_bytes,
+                                       "achieved_GBps": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                                       "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del cwin, cy
+
         # the layer's projections at the prefill length (bf16 in and out, fp32 accumulation)
         for name, (K, N) in (("in_projection", (2048, 8256)), ("out_projection", (4096, 2048))):
             px = torch.randn((T_ROWS, K), device=dev).to(torch.bfloat16)

@@ -475,6 +475,9 @@ gdn_status conv1d_state_step(const gdn_desc *d, const void *x, const void *conv_
             overlap(window, nb, x, xb) || overlap(window, nb, conv_w, wb))
             return GDN_EALIAS;
     }
+    // the kernel moves 8 channels per 16-byte (bf16) or two 16-byte (fp32) pieces
+    if (!aligned(x, 16) || !aligned(conv_w, 16) || !aligned(window, 16) || !aligned(y, 16))
+        return GDN_EINVAL;
     if (launch_conv_step(*d, x, conv_w, window, y, T, stream) != 0) return GDN_EDEVICE;
     return GDN_OK;
 }

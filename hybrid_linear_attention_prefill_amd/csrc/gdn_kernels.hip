@@ -1027,8 +1027,48 @@ __global__ __launch_bounds__(256) void window_kernel(SegArgs sa, const Act *__re
 }
 
 // ------------------------------------------------------------------------------------------
-// conv_step_kernel: standalone causal conv over all channels (window read, not written)
+// conv_step_kernel: standalone causal conv over all channels (window read, not written).
+// Thread t of the grid's x extent takes 8 adjacent channels (one 16-byte load of bf16, two of
+// fp32) over one block of rows, keeping the last three inputs of each channel in registers; a
+// wave reads and writes 64 x 8 contiguous channels of a row per instruction.
 // ------------------------------------------------------------------------------------------
+template <typename Act>
+__device__ __forceinline__ void load8_row(const Act *p, float (&v)[8])
+{
+    if constexpr (sizeof(Act) == 2) {
+        const u32x4 u = *(const u32x4 *)p;
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = __uint_as_float(w[e] << 16);
+            v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    } else {
+        const f32x4 a = *(const f32x4 *)p, b = *(const f32x4 *)(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = a[e];
+            v[4 + e] = b[e];
+        }
+    }
+}
+
+template <typename Out>
+__device__ __forceinline__ void store8_row(Out *p, const float (&v)[8])
+{
+    if constexpr (sizeof(Out) == 2) {
+        u32x4 u;
+        u.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+        u.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+        u.z = (uint32_t)f32_to_bf16_bits(v[4]) | ((uint32_t)f32_to_bf16_bits(v[5]) << 16);
+        u.w = (uint32_t)f32_to_bf16_bits(v[6]) | ((uint32_t)f32_to_bf16_bits(v[7]) << 16);
+        *(u32x4 *)p = u;
+    } else {
+        *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
+        *(f32x4 *)(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+}
+
 template <typename Act, typename Out>
 __global__ __launch_bounds__(256) void conv_step_kernel(const Act *__restrict__ x,
                                                         const Act *__restrict__ w,
@@ -1036,24 +1076,39 @@ __global__ __launch_bounds__(256) void conv_step_kernel(const Act *__restrict__ 
                                                         Out *__restrict__ y, int64_t T, int C,
                                                         int silu, int rows_per_block)
 {
-    const int ch = blockIdx.x * 256 + threadIdx.x;
+    const int ch = 8 * (blockIdx.x * 256 + threadIdx.x);
     if (ch >= C) return;
     const int64_t ra = (int64_t)blockIdx.y * rows_per_block;
     const int64_t rb = min(T, ra + rows_per_block);
-    auto xt = [&](int64_t r) -> float {
-        return r < 0 ? to_f32(win[(3 + r) * C + ch]) : to_f32(x[r * C + ch]);
-    };
-    const float w0 = to_f32(w[ch * 4 + 0]), w1 = to_f32(w[ch * 4 + 1]);
-    const float w2 = to_f32(w[ch * 4 + 2]), w3 = to_f32(w[ch * 4 + 3]);
-    float a0 = xt(ra - 3), a1 = xt(ra - 2), a2 = xt(ra - 1);
+    float wt[8][4];  // taps of channels ch .. ch+7: 32 consecutive values of w
+    {
+        float t[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) load8_row<Act>(w + (int64_t)ch * 4 + 8 * q, *(float(*)[8])(t + 8 * q));
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wt[e][j] = t[4 * e + j];
+    }
+    float a[3][8];  // inputs of rows r-3, r-2, r-1
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+        const int64_t r = ra - 3 + j;
+        load8_row<Act>(r < 0 ? win + (3 + r) * C + ch : x + r * C + ch, a[j]);
+    }
     for (int64_t r = ra; r < rb; ++r) {
-        const float a3 = xt(r);
-        float v = w0 * a0 + w1 * a1 + w2 * a2 + w3 * a3;
-        if (silu) v = v / (1.f + expf(-v));
-        store_out(y + r * C + ch, v);
-        a0 = a1;
-        a1 = a2;
-        a2 = a3;
+        float cur[8], out[8];
+        load8_row<Act>(x + r * C + ch, cur);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float v = wt[e][0] * a[0][e] + wt[e][1] * a[1][e] + wt[e][2] * a[2][e] + wt[e][3] * cur[e];
+            if (silu) v = v / (1.f + expf(-v));
+            out[e] = v;
+            a[0][e] = a[1][e];
+            a[1][e] = a[2][e];
+            a[2][e] = cur[e];
+        }
+        store8_row<Out>(y + r * C + ch, out);
     }
 }
 
@@ -1343,7 +1398,7 @@ static int conv_t(const gdn_desc &d, const void *x, const void *w, void *window,
     const int rpb = 64;
     const int64_t nb = (T + rpb - 1) / rpb;
     if (T > 0) {
-        hipLaunchKernelGGL((conv_step_kernel<Act, Out>), dim3((C + 255) / 256, (unsigned)nb),
+        hipLaunchKernelGGL((conv_step_kernel<Act, Out>), dim3((C / 8 + 255) / 256, (unsigned)nb),
                            dim3(256), 0, st, (const Act *)x, (const Act *)w, (const Act *)window,
                            (Out *)y, T, C, d.conv_silu, rpb);
         // the window becomes rows T .. T+2 of (window ++ x); in place, per channel

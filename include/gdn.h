@@ -272,8 +272,8 @@ int32_t gdn_store_find(const gdn_store *store, uint64_t id);
  * xt = window ++ x; y[t][c] = sum_j conv_w[c][j] * xt[t+j][c] (SiLU if desc->conv_silu);
  * the window becomes the last W-1 rows of xt.  y [T][C] in desc->out_dtype (device),
  * x [T][C] act dtype (device), window [W-1][C] act dtype (device, updated in place).
- * T >= 0; requires conv_width > 0.  y and the window may overlap neither x, conv_w nor each
- * other (GDN_EALIAS). */
+ * T >= 0; requires conv_width > 0.  x, conv_w, window and y must be 16-byte aligned
+ * (GDN_EINVAL).  y and the window may overlap neither x, conv_w nor each other (GDN_EALIAS). */
 gdn_status conv1d_state_step(const gdn_desc *desc, const void *x, const void *conv_w, void *window,
                              void *y, int64_t T, void *stream);
 

@@ -255,6 +255,11 @@ def test_state_ops_validation():
     assert b.lib.conv1d_state_step(ctypes.byref(d), X_, W_, FAKE, X_ + 64, 8, None) == b.GDN_EALIAS
     assert b.lib.conv1d_state_step(ctypes.byref(d), X_, W_, X_ + 16, O_, 8, None) == b.GDN_EALIAS
     assert b.lib.conv1d_state_step(ctypes.byref(d), X_, W_, FAKE, FAKE + 8, 8, None) == b.GDN_EALIAS
+    # every pointer the kernel moves 16-byte pieces through must be 16-byte aligned
+    for i in range(4):
+        args = [X_, W_, FAKE, O_]
+        args[i] += 8
+        assert b.lib.conv1d_state_step(ctypes.byref(d), *args, 8, None) == b.GDN_EINVAL, i
 
 
 def test_commit_rows_exhaustive():

@@ -169,20 +169,35 @@ def test_deterministic_repeat(b):
     assert same_bits(o1, o2) and same_bits(s1.S, s2.S) and same_bits(s1.conv, s2.conv)
 
 
-def test_conv1d_state_step(b):
+@pytest.mark.parametrize("T,out,act,silu", [
+    (70, torch.float32, torch.bfloat16, False),
+    (1000, torch.bfloat16, torch.bfloat16, False),
+    (2, torch.float32, torch.bfloat16, False),
+    (130, torch.float32, torch.float32, True)],
+    ids=["T70_fp32out", "T1000_bf16out", "T2_window_shift", "T130_fp32act_silu"])
+def test_conv1d_state_step(b, T, out, act, silu):
+    """The standalone conv with its window: several 64-row blocks and a ragged last one, bf16
+    and fp32 outputs, fewer rows than the window (the window shifts by T), fp32 activations
+    with SiLU.  Outputs against the float64 conv (fp32 output: fp32 rounding; bf16 output:
+    one bf16 rounding of the fp32 result); the new window bit for bit."""
     shape = synth.LAYER_16x32x128
-    d = _desc(b, shape, out=torch.float32)
-    inp = synth.layer_inputs(shape, 70, seed=7)
+    d = _desc(b, shape, act=act, out=out, conv_silu=silu)
+    inp = synth.layer_inputs(shape, T, seed=7, act_dtype=act)
     from oracle import c_oracle
     rng = np.random.default_rng(0)
-    win0 = synth.cast(rng.standard_normal((3, shape.channels)), torch.bfloat16)
+    win0 = synth.cast(rng.standard_normal((3, shape.channels)), act)
     window = win0.cuda()
-    y = torch.empty((70, shape.channels), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, shape.channels), dtype=out, device="cuda")
     b.conv1d_state_step(d, inp["x"].cuda(), inp["conv_w"].cuda(), window, y)
     torch.cuda.synchronize()
     y_ref, w_ref = c_oracle.causal_conv(synth.f64(inp["x"]), synth.f64(inp["conv_w"]),
-                                        synth.f64(win0))
-    assert rel_l2(y.cpu().numpy(), y_ref) < 1e-6
+                                        synth.f64(win0), silu=silu)
+    yg = y.float().cpu().numpy().astype(np.float64)
+    rms = float(np.sqrt((y_ref ** 2).mean()))
+    rel = 2.0 ** -8 if out == torch.bfloat16 else 1e-6
+    err = np.abs(yg - y_ref) - rel * np.abs(y_ref)
+    assert err.max() <= 1e-6 * rms, ("worst element", np.unravel_index(np.argmax(err), err.shape))
+    assert rel_l2(yg, y_ref) < (2e-3 if out == torch.bfloat16 else 1e-6)
     assert np.array_equal(synth.f64(window), w_ref)
 
 
