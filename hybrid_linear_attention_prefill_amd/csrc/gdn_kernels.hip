@@ -18,9 +18,10 @@
 // at the usual decays, and e^{-G} alone would overflow fp32).
 //
 // Kernels, all launched on the caller's stream:
-//   prep_kernel    grid (sub-chunks, key heads): conv of the q|k channels, L2 norm, K K^T and
-//                  Q K^T on MFMA, and for each value head of the group the cumulative gates,
-//                  Tinv (blocked forward substitution in LDS, fp32) and the decayed mask M.
+//   prep_kernel    one workgroup per (sub-chunk, key head), key head fastest: conv of the
+//                  q|k channels, L2 norm, K K^T and Q K^T on MFMA, and for each value head of
+//                  the group the cumulative gates, Tinv (blocked forward substitution in LDS,
+//                  fp32) and the decayed mask M.
 //                  Everything it writes is independent of the state, so all sub-chunks run
 //                  in parallel.
 //   chain_kernel   grid (d_v tiles of 16, value heads, sequences), 8 waves: the serial walk
@@ -215,7 +216,10 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(SegArgs sa, const Act *__r
 #define TS_OF(hh) ((float *)(ubuf + (2 + (hh)) * MBYTES))
 #define BLK(b, j) (((b) * ((b) + 1) / 2 + (j)) * BSTR)
 
-    const int sub = blockIdx.x, kh = blockIdx.y;
+    // units are numbered key head fastest, so the workgroups that run together read whole rows
+    // of x (every key head's q | k channels of the same sub-chunk) rather than one column slice
+    // of many sub-chunks
+    const int sub = blockIdx.x / Hk, kh = blockIdx.x % Hk;
     const int s = find_seg(sa, sub);
     const int64_t seg_row0 = sa.seg[s].row0;
     const int seg_n = sa.seg[s].n;
@@ -1328,11 +1332,11 @@ static int prefill_t(const gdn_desc &d, const SegArgs &sa, const void *x, const 
     const int conv_on = d.conv_width > 0 ? 1 : 0;
     em.mark(0);
     if (d.conv_silu && conv_on)
-        hipLaunchKernelGGL((prep_kernel<D, Act, true>), dim3(sa.n_sub, d.n_k_heads), dim3(256), 0, st,
+        hipLaunchKernelGGL((prep_kernel<D, Act, true>), dim3((unsigned)(sa.n_sub * d.n_k_heads)), dim3(256), 0, st,
                            sa, (const Act *)x, (const Act *)conv_w, conv_on, g, beta, d.n_k_heads,
                            d.n_v_heads, d.l2_eps, ws);
     else
-        hipLaunchKernelGGL((prep_kernel<D, Act, false>), dim3(sa.n_sub, d.n_k_heads), dim3(256), 0, st,
+        hipLaunchKernelGGL((prep_kernel<D, Act, false>), dim3((unsigned)(sa.n_sub * d.n_k_heads)), dim3(256), 0, st,
                            sa, (const Act *)x, (const Act *)conv_w, conv_on, g, beta, d.n_k_heads,
                            d.n_v_heads, d.l2_eps, ws);
     em.mark(1);
