@@ -103,6 +103,40 @@ def test_nonzero_initial_state_and_window(b):
     assert np.array_equal(synth.f64(s2.conv), w_ref)
 
 
+@pytest.mark.parametrize("case", ["beta_zero", "zero_keys"])
+def test_degenerate_write_strength_and_keys(b, case):
+    """Inputs that write nothing into the state, continued from a non-zero state: beta = 0
+    everywhere, or all key channels zero (rows and window, so every normalised key is exactly
+    zero).  Then each sub-chunk only decays the state: S_T = exp(sum of g) S_0 per value head
+    (the closed form of the rule with its write term gone), and the outputs read the decayed
+    state alone.  Checked against the oracle and against that closed form."""
+    shape = synth.LAYER_16x32x128
+    d = _desc(b, shape, out=torch.float32)
+    Hk, D = shape.n_k_heads, shape.d_k
+    pre = synth.layer_inputs(shape, 128, seed=11)
+    _, s1 = run_fork(b, d, to_dev(pre), new_state(b, d))
+    T = 200
+    inp = synth.layer_inputs(shape, T, seed=12, g_scale=0.01)  # slow decay: S_T stays large
+    if case == "beta_zero":
+        inp["beta"] = torch.zeros_like(inp["beta"])
+    else:
+        inp["x"][:, Hk * D:2 * Hk * D] = 0
+        win = s1.conv.clone()
+        win[:, Hk * D:2 * Hk * D] = 0
+        s1.conv.copy_(win)
+    o2, s2 = run_fork(b, d, to_dev(inp), s1)
+    torch.cuda.synchronize()
+    S1 = s1.S.cpu().numpy().astype(np.float64)
+    o_ref, S_ref, w_ref = oracle(d, inp, S0=S1, window=synth.f64(s1.conv))
+    _check_parity(o2, s2.S, o_ref, S_ref, label=case)
+    decay = np.exp(synth.f64(inp["g"]).sum(axis=0))            # [Hv]
+    S_closed = decay[:, None, None] * S1
+    assert rel_l2(S_ref, S_closed) < 1e-12                       # the oracle meets the closed form
+    Sg = s2.S.cpu().numpy().astype(np.float64)
+    assert np.abs(Sg - S_closed).max() <= 1e-5 * np.abs(S1).max()
+    assert np.array_equal(synth.f64(s2.conv), w_ref)
+
+
 @pytest.mark.parametrize("out", [torch.bfloat16, torch.float32], ids=["bf16_out", "fp32_out"])
 def test_full_layer_8192_all_heads(b, out):
     """The 16/32/128 layer at T=8192 in one call, every value head against the oracle, with
