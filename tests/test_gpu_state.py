@@ -281,6 +281,38 @@ def test_batched_sequences_equal_single_calls(b, desc):
     assert np.array_equal(synth.f64(outs[k].conv.cpu()), w_ref)
 
 
+def test_more_branches_than_one_launch(b, desc):
+    """Forty branches of 1 to 130 rows, from four different states: the host cuts them into
+    launches of at most 32 sequences, and every branch still equals its own single call bit
+    for bit (outputs, final state and window)."""
+    rng = np.random.default_rng(5)
+    lens = [int(n) for n in rng.integers(1, 131, size=40)]
+    total = 256 + sum(lens)
+    inp = synth.layer_inputs(SHAPE, total, seed=33)
+    dinp = to_dev(inp)
+    ws = b.workspace(desc, total, len(lens))
+    starts = [new_state(b, desc)]
+    for r in (64, 128, 256):
+        starts.append(run_fork(b, desc, dinp, new_state(b, desc), rows=(0, r), ws=ws)[1])
+    inits = [starts[k % 4] for k in range(len(lens))]
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    rows = slice(256, total)
+    o = torch.empty((cu[-1], 32, 128), dtype=torch.bfloat16, device="cuda")
+    outs = [b.State(desc) for _ in lens]
+    b.gdn_prefill_branches(desc, cu, dinp["x"][rows], dinp["conv_w"], dinp["g"][rows],
+                           dinp["beta"][rows], inits, outs, o, ws)
+    torch.cuda.synchronize()
+    for k, n in enumerate(lens):
+        r0 = 256 + cu[k]
+        of, sf = run_fork(b, desc, dinp, inits[k], rows=(r0, r0 + n), ws=ws)
+        torch.cuda.synchronize()
+        assert same_bits(o[cu[k]:cu[k + 1]], of), k
+        assert same_bits(outs[k].S, sf.S) and same_bits(outs[k].conv, sf.conv), k
+        assert outs[k].pos == inits[k].pos + n
+
+
 def test_refusals_enqueue_nothing(b, desc):
     dinp = to_dev(synth.layer_inputs(SHAPE, 128, seed=40))
     ws = b.workspace(desc, 128)
