@@ -44,6 +44,34 @@ def test_one_call_is_one_launch_of_all_sub_chunks():
                          S_out=sout.S.ctypes.data, win_out=sout.conv.ctypes.data)]
 
 
+def test_calls_that_absorb_no_rows_copy_the_state_and_launch_nothing():
+    """A FORK of zero rows, and a COMMIT of fewer rows than the grid (the whole call is the
+    pending tail), absorb nothing: they enqueue no kernel, touch no input pointer (the inputs
+    may even be null), and leave the output state equal to the input state, copied bit for bit
+    when they are distinct buffers."""
+    d = layer_desc()
+    live = HostState(d, fill=True, seed=3)
+    live.c.pos = 1024
+    for mode, T in ((b.GDN_FORK, 0), (b.GDN_COMMIT, 0), (b.GDN_COMMIT, 511)):
+        out = HostState(d, fill=True, seed=4)
+        b.reset()
+        rows = ctypes.c_int64(-1)
+        st = b.lib.gdn_prefill_chunked(ctypes.byref(d), None, None, None, None, live.ref(),
+                                       out.ref(), None, T, mode, ctypes.byref(rows), None, 0, None)
+        assert st == b.GDN_OK and rows.value == 0, (mode, T, st)
+        assert [k for k, _, _ in b.launches() if k == b.KIND_PREFILL] == []
+        assert np.array_equal(out.S.view(np.int32), live.S.view(np.int32))
+        assert np.array_equal(out.conv, live.conv)
+        assert out.c.pos == 1024 and out.c.tag == live.c.tag
+    # in place: a commit of a pending tail only leaves the state as it was
+    before = live.S.copy()
+    rows = ctypes.c_int64(-1)
+    assert b.lib.gdn_prefill_chunked(ctypes.byref(d), None, None, None, None, live.ref(), live.ref(),
+                                     None, 300, b.GDN_COMMIT, ctypes.byref(rows), None, 0,
+                                     None) == b.GDN_OK
+    assert rows.value == 0 and live.c.pos == 1024 and np.array_equal(live.S, before)
+
+
 @pytest.mark.parametrize("cap,T", [(256, 1000), (64, 200), (512, 1024)])
 def test_long_sequence_runs_as_chained_launches(monkeypatch, cap, T):
     """A sequence longer than the per-launch row cap runs as launches that each start at a
