@@ -21,10 +21,12 @@ Prints one JSON line with those rates, a roofline object for the dominant kernel
 the layer's algorithmic bytes over its average duration in the timed steps) and for the whole
 call, the other workloads (the one-head fp32 layer; the multi-turn replay with forks; the
 24-layer long session with checkpoints and a divergence; 32 batched branches against one
-prefill per branch), and the float64 CPU oracle timed on bounded samples.
+prefill per branch), the rows beside the layer (`extras`: state capture/restore, a 370-row
+fork, decode steps of 1 and 32 sessions, the standalone conv, the two projections and the
+full-attention layer), and the float64 CPU oracle timed on bounded samples.
 
-    --extras                also time state capture/restore, a 370-row fork, decode steps
-                            of 1 and 32 sessions, the two projections and the attention layer
+    --no-extras             skip the rows beside the layer (`--extras` is accepted and is the
+                            default)
     --no-workloads          skip the one-head and session workloads
     --copy-calibration N    run a plain N-byte device copy after timing (for counter scaling)
 """
@@ -452,9 +454,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--extras", action="store_true",
-                    help="also time state capture/restore, a 370-row fork, decode "
-                         "steps of 1 and 32 sessions, the two projections and the full-attention "
-                         "layer")
+                    help="time the rows beside the layer (the default): state capture/restore, "
+                         "a 370-row fork, decode steps of 1 and 32 sessions, the standalone conv, "
+                         "the two projections and the full-attention layer")
+    ap.add_argument("--no-extras", action="store_true", help="skip the rows beside the layer")
     ap.add_argument("--peaks", action="store_true",
                     help="also measure a device copy and torch's bf16 matmul at the projection "
                          "shapes, as reference rates")
@@ -557,7 +560,7 @@ def main():
     warm_ms = ev0.elapsed_time(ev1) / args.steps
 
     extras = {}
-    if args.extras:
+    if not args.no_extras:
         # state copies (capture + restore of the 2 MiB state and window) and a fork of a
         # 330-row pending tail plus a 40-row question above the committed rows
         snap = b.State(desc)
