@@ -369,7 +369,9 @@ gdn_status gdn_prefill_branches(const gdn_desc *desc, int32_t B, const int64_t *
  * to fp32 rounding; it is not bitwise a GDN_FORK prefill of the same row, whose chunk
  * algebra rounds differently.  One kernel per group of at most 32 sequences, plus a
  * window-shift kernel when some out[b] shares its window with in[b] (in place): ping-pong
- * between two states per session to keep one launch per step. */
+ * between two states per session to keep one launch per step.  The call enqueues kernels
+ * only (no copy, fill or synchronisation), so a serving loop can capture a run of steps in a
+ * HIP graph and replay it; the host-side pos fields then advance only with eager calls. */
 gdn_status gdn_decode_step(const gdn_desc *desc, int32_t B, const void *x, const void *conv_w,
                            const float *g, const float *beta, const gdn_state *const *in,
                            gdn_state *const *out, void *o, void *stream);
