@@ -36,6 +36,7 @@ import json
 import os
 import sys
 import time
+import traceback
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -560,155 +561,165 @@ def main():
     warm_ms = ev0.elapsed_time(ev1) / args.steps
 
     extras = {}
-    if not args.no_extras:
-        # state copies (capture + restore of the 2 MiB state and window) and a fork of a
-        # 330-row pending tail plus a 40-row question above the committed rows
-        snap = b.State(desc)
-        fork_out = b.State(desc)
-        fo = torch.empty((370, Hv, d), dtype=torch.bfloat16, device=dev)
-        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps2 = 20
-        e2.record(stream)
-        for _ in range(reps2):
-            b.gdn_state_capture(desc, state, snap)
-            b.gdn_state_restore(desc, state, snap)
-        e3.record(stream)
-        torch.cuda.synchronize()
-        copy_ms = e2.elapsed_time(e3) / reps2
-        copy_bytes = 2 * 2 * (b.gdn_state_S_bytes(desc) + b.gdn_state_conv_bytes(desc))
-        e2.record(stream)
-        for _ in range(reps2):
-            s = sets[0]
-            b.gdn_prefill_chunked(desc, s["x"][:370], s["conv_w"], s["g"][:370], s["beta"][:370],
-                                  state, fork_out, fo, 370, b.GDN_FORK, ws)
-        e3.record(stream)
-        torch.cuda.synchronize()
-        extras = {"state_capture_restore_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
-                  "fork_370_rows_ms": round(e2.elapsed_time(e3) / reps2, 4)}
-        # decode steps of B sessions, each from its own forked state, in place: the step
-        # streams every session's fp32 state in and out, so it is HBM-bound for large B
-        C = desc.channels
-        # (two states per session, stepped back and forth: one launch per step)
-        for B in (1, 32):
-            ping = [b.State(desc) for _ in range(B)]
-            pong = [b.State(desc) for _ in range(B)]
-            for st_ in ping:
-                b.gdn_state_capture(desc, state, st_)
-            s = sets[0]
-            xb, gb, bb = s["x"][:B].contiguous(), s["g"][:B].contiguous(), s["beta"][:B].contiguous()
-            ob = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
-            for i in range(4):
-                src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
-                b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
-            reps3 = 50
+    # The rows beside the layer are reported, not the headline: a failure among them is
+    # recorded in the line (and printed) instead of losing the layer's measurement.
+    try:
+        if not args.no_extras:
+            # state copies (capture + restore of the 2 MiB state and window) and a fork of a
+            # 330-row pending tail plus a 40-row question above the committed rows
+            snap = b.State(desc)
+            fork_out = b.State(desc)
+            fo = torch.empty((370, Hv, d), dtype=torch.bfloat16, device=dev)
+            e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps2 = 20
             e2.record(stream)
-            for i in range(reps3):
-                src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
-                b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
+            for _ in range(reps2):
+                b.gdn_state_capture(desc, state, snap)
+                b.gdn_state_restore(desc, state, snap)
             e3.record(stream)
             torch.cuda.synchronize()
-            step_ms = e2.elapsed_time(e3) / reps3
-            # the same steps as a serving loop runs them: captured once in a HIP graph and
-            # replayed, so that no host launch sits between two steps
-            graph = torch.cuda.CUDAGraph()
-            side = torch.cuda.Stream()
-            side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(side):
-                with torch.cuda.graph(graph, stream=side):
-                    for i in range(reps3):
-                        src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
-                        b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
-            torch.cuda.synchronize()
-            graph.replay()
+            copy_ms = e2.elapsed_time(e3) / reps2
+            copy_bytes = 2 * 2 * (b.gdn_state_S_bytes(desc) + b.gdn_state_conv_bytes(desc))
             e2.record(stream)
-            graph.replay()
+            for _ in range(reps2):
+                s = sets[0]
+                b.gdn_prefill_chunked(desc, s["x"][:370], s["conv_w"], s["g"][:370], s["beta"][:370],
+                                      state, fork_out, fo, 370, b.GDN_FORK, ws)
             e3.record(stream)
             torch.cuda.synchronize()
-            graph_ms = e2.elapsed_time(e3) / reps3
-            del graph
-            step_bytes = B * (2 * Hv * d * d * 4 + 2 * 3 * C * 2 + C * 2 + 2 * Hv * 4 + Hv * d * 2)
-            gbps = step_bytes / (step_ms * 1e-3) / 1e9
-            ggbps = step_bytes / (graph_ms * 1e-3) / 1e9
-            extras["decode_B%d" % B] = {
-                "us_per_step": round(step_ms * 1e3, 2),
-                "tokens_per_s": round(B / (step_ms * 1e-3), 1),
-                "algorithmic_bytes_per_step": step_bytes,
-                "achieved_GBps": round(gbps, 1),
-                "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
-                "us_per_step_graph": round(graph_ms * 1e3, 2),
-                "tokens_per_s_graph": round(B / (graph_ms * 1e-3), 1),
-                "hbm_frac_graph": round(ggbps / HBM_PEAK_GBS, 4)}
-            del ping, pong
+            extras = {"state_capture_restore_GBps": round(copy_bytes / (copy_ms * 1e-3) / 1e9, 1),
+                      "fork_370_rows_ms": round(e2.elapsed_time(e3) / reps2, 4)}
+            # decode steps of B sessions, each from its own forked state, in place: the step
+            # streams every session's fp32 state in and out, so it is HBM-bound for large B
+            C = desc.channels
+            # (two states per session, stepped back and forth: one launch per step)
+            for B in (1, 32):
+                ping = [b.State(desc) for _ in range(B)]
+                pong = [b.State(desc) for _ in range(B)]
+                for st_ in ping:
+                    b.gdn_state_capture(desc, state, st_)
+                s = sets[0]
+                xb, gb, bb = s["x"][:B].contiguous(), s["g"][:B].contiguous(), s["beta"][:B].contiguous()
+                ob = torch.empty((B, Hv, d), dtype=torch.bfloat16, device=dev)
+                for i in range(4):
+                    src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
+                    b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
+                reps3 = 50
+                e2.record(stream)
+                for i in range(reps3):
+                    src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
+                    b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
+                e3.record(stream)
+                torch.cuda.synchronize()
+                step_ms = e2.elapsed_time(e3) / reps3
+                # the same steps as a serving loop runs them: captured once in a HIP graph and
+                # replayed, so that no host launch sits between two steps
+                graph = torch.cuda.CUDAGraph()
+                side = torch.cuda.Stream()
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    with torch.cuda.graph(graph, stream=side):
+                        for i in range(reps3):
+                            src, dst = (ping, pong) if i % 2 == 0 else (pong, ping)
+                            b.gdn_decode_step(desc, xb, s["conv_w"], gb, bb, src, dst, ob)
+                torch.cuda.synchronize()
+                graph.replay()
+                e2.record(stream)
+                graph.replay()
+                e3.record(stream)
+                torch.cuda.synchronize()
+                graph_ms = e2.elapsed_time(e3) / reps3
+                del graph
+                step_bytes = B * (2 * Hv * d * d * 4 + 2 * 3 * C * 2 + C * 2 + 2 * Hv * 4 + Hv * d * 2)
+                gbps = step_bytes / (step_ms * 1e-3) / 1e9
+                ggbps = step_bytes / (graph_ms * 1e-3) / 1e9
+                extras["decode_B%d" % B] = {
+                    "us_per_step": round(step_ms * 1e3, 2),
+                    "tokens_per_s": round(B / (step_ms * 1e-3), 1),
+                    "algorithmic_bytes_per_step": step_bytes,
+                    "achieved_GBps": round(gbps, 1),
+                    "hbm_frac": round(gbps / HBM_PEAK_GBS, 4),
+                    "us_per_step_graph": round(graph_ms * 1e3, 2),
+                    "tokens_per_s_graph": round(B / (graph_ms * 1e-3), 1),
+                    "hbm_frac_graph": round(ggbps / HBM_PEAK_GBS, 4)}
+                del ping, pong
 
-        # the standalone conv with its window over the layer's channels (bf16 in and out)
-        cx = sets[0]["x"]
-        cwin = torch.zeros((3, cx.shape[1]), dtype=torch.bfloat16, device=dev)
-        cy = torch.empty_like(cx)
-        warm_clock(lambda: b.conv1d_state_step(desc, cx, sets[0]["conv_w"], cwin, cy), 0.1)
-        reps6 = 20
-        e2.record(stream)
-        for _ in range(reps6):
-            b.conv1d_state_step(desc, cx, sets[0]["conv_w"], cwin, cy)
-        e3.record(stream)
-        torch.cuda.synchronize()
-        conv_ms = e2.elapsed_time(e3) / reps6
-        conv_bytes = 2 * cx.numel() * 2 + 4 * cx.shape[1] * 2 + 2 * 3 * cx.shape[1] * 2
-        extras["conv1d_state_step"] = {"T": T_ROWS, "channels": int(cx.shape[1]),
-                                       "us": round(conv_ms * 1e3, 2),
-                                       "algorithmic_bytes": conv_bytes,
-                                       "achieved_GBps": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
-                                       "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        del cwin, cy
-
-        # the layer's projections at the prefill length (bf16 in and out, fp32 accumulation)
-        for name, (K, N) in (("in_projection", (2048, 8256)), ("out_projection", (4096, 2048))):
-            px = torch.randn((T_ROWS, K), device=dev).to(torch.bfloat16)
-            pw = (torch.randn((N, K), device=dev) / K ** 0.5).to(torch.bfloat16)
-            py = torch.empty((T_ROWS, N), dtype=torch.bfloat16, device=dev)
-            warm_clock(lambda: b.gdn_linear(px, pw, py))
-            reps4 = 50
+            # the standalone conv with its window over the layer's channels (bf16 in and out)
+            cx = sets[0]["x"]
+            cwin = torch.zeros((3, cx.shape[1]), dtype=torch.bfloat16, device=dev)
+            cy = torch.empty_like(cx)
+            warm_clock(lambda: b.conv1d_state_step(desc, cx, sets[0]["conv_w"], cwin, cy), 0.1)
+            reps6 = 20
             e2.record(stream)
-            for _ in range(reps4):
-                b.gdn_linear(px, pw, py)
+            for _ in range(reps6):
+                b.conv1d_state_step(desc, cx, sets[0]["conv_w"], cwin, cy)
             e3.record(stream)
             torch.cuda.synchronize()
-            lin_ms = e2.elapsed_time(e3) / reps4
-            tflops = 2.0 * T_ROWS * K * N / (lin_ms * 1e-3) / 1e12
-            extras["linear_" + name] = {"T": T_ROWS, "K": K, "N": N,
-                                        "us": round(lin_ms * 1e3, 2),
-                                        "tflops": round(tflops, 1),
-                                        "mfma_bf16_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
-            del px, pw, py
+            conv_ms = e2.elapsed_time(e3) / reps6
+            conv_bytes = 2 * cx.numel() * 2 + 4 * cx.shape[1] * 2 + 2 * 3 * cx.shape[1] * 2
+            extras["conv1d_state_step"] = {"T": T_ROWS, "channels": int(cx.shape[1]),
+                                           "us": round(conv_ms * 1e3, 2),
+                                           "algorithmic_bytes": conv_bytes,
+                                           "achieved_GBps": round(conv_bytes / (conv_ms * 1e-3) / 1e9, 1),
+                                           "hbm_frac": round(conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            del cwin, cy
 
-        # the hybrid's full-attention layer at the same length: 16 query heads over 2 key
-        # heads of width 256, causal over 8,192 rows (flops: QK^T and PV over the causal
-        # triangle, 4 D per query-key pair)
-        Hq_a, Hkv_a, D_a = 16, 2, 256
-        aq = torch.randn((T_ROWS, Hq_a, D_a), device=dev).to(torch.bfloat16)
-        ak = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
-        av = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
-        ao = torch.empty_like(aq)
-        adesc = b.make_attn_desc(Hq_a, Hkv_a, D_a)
-        warm_clock(lambda: b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)]))
-        reps5 = 20
-        e2.record(stream)
-        for _ in range(reps5):
-            b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)])
-        e3.record(stream)
-        torch.cuda.synchronize()
-        att_ms = e2.elapsed_time(e3) / reps5
-        att_flops = 4.0 * D_a * Hq_a * T_ROWS * (T_ROWS + 1) / 2
-        att_tf = att_flops / (att_ms * 1e-3) / 1e12
-        extras["attention_prefill"] = {"T": T_ROWS, "n_q_heads": Hq_a, "n_kv_heads": Hkv_a,
-                                       "head_dim": D_a, "us": round(att_ms * 1e3, 1),
-                                       "tflops": round(att_tf, 1),
-                                       "mfma_bf16_frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4)}
-        del aq, ak, av, ao
+            # the layer's projections at the prefill length (bf16 in and out, fp32 accumulation)
+            for name, (K, N) in (("in_projection", (2048, 8256)), ("out_projection", (4096, 2048))):
+                px = torch.randn((T_ROWS, K), device=dev).to(torch.bfloat16)
+                pw = (torch.randn((N, K), device=dev) / K ** 0.5).to(torch.bfloat16)
+                py = torch.empty((T_ROWS, N), dtype=torch.bfloat16, device=dev)
+                warm_clock(lambda: b.gdn_linear(px, pw, py))
+                reps4 = 50
+                e2.record(stream)
+                for _ in range(reps4):
+                    b.gdn_linear(px, pw, py)
+                e3.record(stream)
+                torch.cuda.synchronize()
+                lin_ms = e2.elapsed_time(e3) / reps4
+                tflops = 2.0 * T_ROWS * K * N / (lin_ms * 1e-3) / 1e12
+                extras["linear_" + name] = {"T": T_ROWS, "K": K, "N": N,
+                                            "us": round(lin_ms * 1e3, 2),
+                                            "tflops": round(tflops, 1),
+                                            "mfma_bf16_frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4)}
+                del px, pw, py
+
+            # the hybrid's full-attention layer at the same length: 16 query heads over 2 key
+            # heads of width 256, causal over 8,192 rows (flops: QK^T and PV over the causal
+            # triangle, 4 D per query-key pair)
+            Hq_a, Hkv_a, D_a = 16, 2, 256
+            aq = torch.randn((T_ROWS, Hq_a, D_a), device=dev).to(torch.bfloat16)
+            ak = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
+            av = torch.randn((T_ROWS, Hkv_a, D_a), device=dev).to(torch.bfloat16)
+            ao = torch.empty_like(aq)
+            adesc = b.make_attn_desc(Hq_a, Hkv_a, D_a)
+            warm_clock(lambda: b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)]))
+            reps5 = 20
+            e2.record(stream)
+            for _ in range(reps5):
+                b.gdn_attention_prefill(adesc, [(aq, ak, av, ao, 0)])
+            e3.record(stream)
+            torch.cuda.synchronize()
+            att_ms = e2.elapsed_time(e3) / reps5
+            att_flops = 4.0 * D_a * Hq_a * T_ROWS * (T_ROWS + 1) / 2
+            att_tf = att_flops / (att_ms * 1e-3) / 1e12
+            extras["attention_prefill"] = {"T": T_ROWS, "n_q_heads": Hq_a, "n_kv_heads": Hkv_a,
+                                           "head_dim": D_a, "us": round(att_ms * 1e3, 1),
+                                           "tflops": round(att_tf, 1),
+                                           "mfma_bf16_frac": round(att_tf / MFMA_F16_PEAK_TFLOPS, 4)}
+            del aq, ak, av, ao
+    except Exception as e:  # noqa: BLE001
+        traceback.print_exc()
+        extras["error"] = repr(e)[:300]
 
     workloads = None
     if not args.no_workloads:
-        workloads = {"one_head_fp32_T1024": one_head_rate(b, synth, dev)}
-        workloads.update(session_workloads(b, synth, desc, dev, shape))
+        try:
+            workloads = {"one_head_fp32_T1024": one_head_rate(b, synth, dev)}
+            workloads.update(session_workloads(b, synth, desc, dev, shape))
+        except Exception as e:  # noqa: BLE001
+            traceback.print_exc()
+            workloads = {"error": repr(e)[:300]}
     if args.peaks:
         extras["measured_peaks"] = measured_peaks(dev)
 
