@@ -10,15 +10,24 @@
 // accumulator are rescaled by exp(old max - new max), and the split's exponentials, rounded to
 // bf16, are added with their value rows.  Split boundaries are absolute multiples of 256 and
 // every row's arithmetic is the same whichever call, tile or lane it lands in.  Keys past a
-// row's own position are masked to an exact zero weight; a 64-key block that is masked for
-// every row of a workgroup is skipped, which changes nothing (x + 0 and x * 1 are exact).
+// row's own position are masked to an exact zero weight, and keys past the cache end read as
+// zero, so every block of a workgroup's last split can be run whole: a block masked for every
+// row adds exact zeros (x + 0 and x * 1 are exact).
 //
 // Workgroup: 8 waves, each owning 16 query rows of one query head; the waves share the key
 // head, so one 64-key block of K or V staged in LDS serves all of them.  For each split the
 // waves first form S^T = K Q^T for its 256 keys (16 x 256 scores per wave, in registers), then
 // the softmax update, then O^T += V^T P^T.  Both products put a query row in lane % 16, so the
-// row statistics and the rescaling stay inside a lane.  K and V blocks stream through a ring
-// of three LDS slots, loaded two blocks ahead.
+// row statistics and the rescaling stay inside a lane.
+//
+// Staging: a split is eight block steps (its four K blocks, then its four V blocks), and block
+// e of a split lives in LDS slot e mod 4, four separate arrays, so every step reads a slot
+// known at compile time.  Each step first issues the copy of the block three steps ahead into
+// the slot the previous step read, straight from global memory into LDS (buffer loads with the
+// LDS bit: no registers, no LDS write instructions), then runs its products, then waits until
+// this wave's copies of the next step's block have landed (the two later blocks' copies may
+// still be in flight) and meets the other waves at a barrier.  The compiler tells the four
+// slots apart, so the products' LDS reads never wait for copies bound for other slots.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -40,7 +49,6 @@ constexpr int kSplit = 256;  // key positions per split
 constexpr int kBlk = 64;     // keys per LDS block
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRing = 3;
 
 // An LDS block holds 64 key rows of D bf16 (R = D / 8 chunks of 16 bytes per row), in one of two
 // layouts of the same size; in both, every fragment address is one per-lane base plus a
@@ -73,43 +81,6 @@ __device__ __forceinline__ int k_row_start(int t)
 __device__ __forceinline__ int sigma(int r) { return ((r & 7) << 1) | (r >> 3); }
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-
-// Byte offsets of this thread's chunks of a 64-key block of key head kvh in a [rows][Hkv][D]
-// cache, relative to the block's first key: chunk i is row id / (D / 8), 16-byte column
-// id % (D / 8), with id = tid + 512 i.  Constant for the whole call.
-template <int D>
-__device__ __forceinline__ void blk_offsets(int Hkv, int kvh, int tid, uint32_t (&off)[D / 64])
-{
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-        const int id = tid + kThreads * i, row = id / (D / 8), pc = id % (D / 8);
-        off[i] = (uint32_t)(((row * Hkv + kvh) * D + 8 * pc) * 2);
-    }
-}
-
-// One 64-key block (keys key0 .. key0 + 63) into registers, through a buffer resource that
-// covers keys key0 .. L - 1 only: its range check reads keys at or past L as zero, so the loads
-// need no compare and no branch.  key0 < L.
-template <int D>
-__device__ __forceinline__ void blk_load(const uint16_t *base, int64_t key0, int64_t L, int Hkv,
-                                         const uint32_t (&off)[D / 64], u32x4 (&v)[D / 64])
-{
-    const int64_t nk = L - key0 < kBlk ? L - key0 : kBlk;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(base + key0 * Hkv * D), 0, (int)(nk * Hkv * D * 2), kRsrcWord3);
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off[i], 0, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void blk_store(u32x4 *slot, int tid, const u32x4 (&v)[D / 64], bool isv)
-{
-#pragma unroll
-    for (int i = 0; i < D / 64; ++i) {
-        const int id = tid + kThreads * i, row = id / (D / 8), pc = id % (D / 8);
-        slot[(isv ? row * kRowChunks<D> : k_row_start<D>(row)) + pc] = v[i];
-    }
-}
 
 // K fragment (A operand of S^T = K Q^T) for tile q4 and d-step ks: lane (r = lane % 16, g)
 // holds K[16 q4 + sigma(r)][32 ks + 8 g .. + 7].  kbase = the lane's slot offset of
@@ -152,30 +123,51 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v)
     *(u32x2 *)p = __builtin_bit_cast(u32x2, h);
 }
 
-// The next block to stage: (split j, V or K, block k within the split).
-struct Cursor {
-    int j, isv, k;
-};
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void advance(Cursor &c, int ns, int nk_last)
+// A block's kSlotChunks<D> 16-byte chunks are filled by kNGI copy instructions of 64 lanes
+// (lane i of instruction gi fills chunk 64 gi + i); wave w issues instructions w, w + 8, ...:
+// kJ of them, or kJ - 1 in waves past kNGI mod 8.
+template <int D>
+constexpr int kNGI = kSlotChunks<D> / 64;
+template <int D>
+constexpr int kJ = (kNGI<D> + kWaves - 1) / kWaves;
+static_assert(kSlotChunks<128> % 64 == 0 && kSlotChunks<256> % 64 == 0, "whole copy instructions");
+
+// Byte offset, from the block's first key, of what chunk p of a slot holds: key row and 16-byte
+// column in the paired-row (K) or padded-row (V) layout; pad chunks take column 0 of their row.
+template <int D>
+__device__ __forceinline__ uint32_t dma_off(int p, bool isv, int Hkv, int kvh)
 {
-    const int nk = c.j == ns - 1 ? nk_last : kSplit / kBlk;
-    if (++c.k == nk) {
-        c.k = 0;
-        if (c.isv) {
-            c.isv = 0;
-            ++c.j;
-        } else {
-            c.isv = 1;
-        }
+    constexpr int R = D / 8;
+    int row, c;
+    if (isv) {
+        row = p / (R + 1);
+        c = p % (R + 1);
+        if (c == R) c = 0;
+    } else {
+        const int pair = p / kPairChunks<D>, q = p % kPairChunks<D>;
+        row = 2 * pair + (q >= R && q < 2 * R ? 1 : 0);
+        c = q < R ? q : (q < 2 * R ? q - R : 0);
     }
+    if (row > kBlk - 1) row = kBlk - 1;  // offsets of copies a wave does not issue
+    return (uint32_t)(((row * Hkv + kvh) * D + 8 * c) * 2);
+}
+
+// One 16-byte-per-lane copy from a buffer resource straight into 1 KB of LDS at dst (lane i's
+// 16 bytes at dst + 16 i); reads outside the resource's range give zeros.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, u32x4 *dst, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, 0);
 }
 
 template <int D, typename Out>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int Hkv, int HW,
                                                         float c2)
 {
-    __shared__ u32x4 ring[kRing][kSlotChunks<D>];
+    __shared__ u32x4 slot0[kSlotChunks<D>], slot1[kSlotChunks<D>], slot2[kSlotChunks<D>],
+        slot3[kSlotChunks<D>];
+    __shared__ u32x4 scratch_lds[64];  // where the copies of blocks past the last split go
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const int RW = kWaves / HW;  // 16-row tiles per workgroup
@@ -199,12 +191,16 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     const int64_t t_end = t0 + 16 * RW < T ? t0 + 16 * RW : T;
     const int64_t p_last = pos0 + t_end - 1;   // last valid row of the workgroup
     const int ns = (int)(p_last / kSplit) + 1;
-    const int nk_last = (int)((p_last % kSplit) / kBlk) + 1;
     const int64_t trow = tw + li, prow = pos0 + trow;
 
     const uint16_t *kp = (const uint16_t *)sq.k, *vp = (const uint16_t *)sq.v;
-    uint32_t boff[D / 64];
-    blk_offsets<D>(Hkv, kvh, tid, boff);
+    uint32_t offk[kJ<D>], offv[kJ<D>];  // this lane's copy offsets, the same for every block
+#pragma unroll
+    for (int i = 0; i < kJ<D>; ++i) {
+        const int p = 64 * (wave + kWaves * i) + lane;
+        offk[i] = dma_off<D>(p, false, Hkv, kvh);
+        offv[i] = dma_off<D>(p, true, Hkv, kvh);
+    }
     const int kbase = k_row_start<D>(sigma(li)) + g;
     const int j4 = lane & 15;
     const int vbase = 16 * sigma(4 * g + j4 / 4) * kRowChunks<D> + 8 * (j4 % 4);
@@ -230,71 +226,94 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     float m = -__builtin_inff();
     const int64_t p_wave = pos0 + tw;  // the wave's first (smallest) row position
 
-    // prologue: blocks 0 and 1 into slots 0 and 1
-    Cursor ld = {0, 0, 0};
-    u32x4 stage[D / 64];
+    // Block q = 8 j + e: e < 4 the K block e of split j, else its V block e - 4; it lives in
+    // slot q mod 4.  Blocks of splits past the last go to the scratch kilobyte (zeros), so that
+    // every wave issues the same copies at every step.
+    auto dma = [&](u32x4 *slot, int q) {
+        const int j = q >> 3, e = q & 7;
+        const bool isv = e >= 4;
+        const int64_t key0 = (int64_t)kSplit * j + kBlk * (e & 3);
+        const bool real = j < ns;
+        const int64_t nk = real && key0 < L ? (L - key0 < kBlk ? L - key0 : kBlk) : 0;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)((isv ? vp : kp) + (real ? key0 : 0) * Hkv * D), 0, (int)(nk * Hkv * D * 2),
+            kRsrcWord3);
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        if (ld.j < ns) {
-            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, boff, stage);
-            blk_store<D>(ring[b], tid, stage, ld.isv != 0);
-            advance(ld, ns, nk_last);
+        for (int i = 0; i < kJ<D>; ++i) {
+            const int gi = wave + kWaves * i;
+            // wave-uniform: the last round only in the waves below kNGI mod 8
+            if (i + 1 < kJ<D> || kNGI<D> % kWaves == 0 || gi < kNGI<D>) {
+                u32x4 *dst = real ? slot + 64 * gi : scratch_lds;
+                copy_to_lds(r, dst, isv ? offv[i] : offk[i]);
+            }
         }
-    }
-    __syncthreads();
-    int rs = 0;
-
-    // One block step: stage the block two ahead, run `work` on slot rs, store, barrier.
-    auto step = [&](auto &&work) {
-        const bool more = ld.j < ns;
-        if (more)
-            blk_load<D>(ld.isv ? vp : kp, (int64_t)kSplit * ld.j + kBlk * ld.k, L, Hkv, boff, stage);
-        work(ring[rs]);
-        if (more) {
-            blk_store<D>(ring[rs == 0 ? 2 : rs - 1], tid, stage, ld.isv != 0);
-            advance(ld, ns, nk_last);
+    };
+    // this wave's copies of the next step's block have landed (those of the two blocks after it
+    // may still be in flight; the counter drops in issue order), then the workgroup meets
+    auto meet = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's copies per block: kJ, or kJ - 1 for waves past NGI mod 8
+        const bool full_round =
+            kNGI<D> % kWaves == 0 || __builtin_amdgcn_readfirstlane(wave) < kNGI<D> % kWaves;
+        if constexpr (kJ<D> == 5) {
+            if (full_round) __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
+            else __builtin_amdgcn_s_waitcnt(0x0F78);             // vmcnt(8)
+        } else {
+            if (full_round) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
+            else __builtin_amdgcn_s_waitcnt(0x0F74);             // vmcnt(4)
         }
-        __syncthreads();
-        rs = rs == kRing - 1 ? 0 : rs + 1;
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
     };
 
+    dma(slot0, 0);
+    dma(slot1, 1);
+    dma(slot2, 2);
+    meet();
+
     for (int j = 0; j < ns; ++j) {
-        const int nk = j == ns - 1 ? nk_last : kSplit / kBlk;
         f32x4 S[kSplit / 16];  // S^T tiles: lane (row li, g) holds keys 16 kt + sigma(4 g + i)
+        auto kstep = [&](const u32x4 *slot, int kc) {
+            // fragments of d-step ks + 1 are read while step ks multiplies
+            bf16x8 kf[2][4];
 #pragma unroll
-        for (int kc = 0; kc < kSplit / kBlk; ++kc) {
+            for (int q4 = 0; q4 < 4; ++q4) kf[0][q4] = k_frag<D>(slot, kbase, q4, 0);
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) S[4 * kc + q4] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kc < nk)
-                step([&](const u32x4 *slot) {
-                    // fragments of d-step ks + 1 are read while step ks multiplies
-                    bf16x8 kf[2][4];
+            for (int ks = 0; ks < D / 32; ++ks) {
+                if (ks + 1 < D / 32)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) kf[0][q4] = k_frag<D>(slot, kbase, q4, 0);
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        kf[(ks + 1) & 1][q4] = k_frag<D>(slot, kbase, q4, ks + 1);
 #pragma unroll
-                    for (int ks = 0; ks < D / 32; ++ks) {
-                        if (ks + 1 < D / 32)
-#pragma unroll
-                            for (int q4 = 0; q4 < 4; ++q4)
-                                kf[(ks + 1) & 1][q4] = k_frag<D>(slot, kbase, q4, ks + 1);
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4)
-                            S[4 * kc + q4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                kf[ks & 1][q4], qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[4 * kc + q4],
-                                0, 0, 0);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                });
-        }
+                for (int q4 = 0; q4 < 4; ++q4)
+                    S[4 * kc + q4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        kf[ks & 1][q4], qf[ks], ks == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : S[4 * kc + q4],
+                        0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        const int q0 = 8 * j;
+        dma(slot3, q0 + 3);
+        kstep(slot0, 0);
+        meet();
+        dma(slot0, q0 + 4);
+        kstep(slot1, 1);
+        meet();
+        dma(slot1, q0 + 5);
+        kstep(slot2, 2);
+        meet();
+        dma(slot2, q0 + 6);
+        kstep(slot3, 3);
+        meet();
 
         // softmax update for split j (scores in units of log2: s * c2).  Key 16 kt + sigma(4 g
-        // + i) of the split is live for this row when it is at most lim: not past the row's
-        // own position, and inside a staged block.  When every key of the split is live for
-        // every row of the wave, nothing is masked.
+        // + i) of the split is live for this row when it is at most lim, the row's own
+        // position; when every key of the split is at or below every row of the wave, nothing
+        // is masked.
         const int64_t key_base = (int64_t)kSplit * j;
         const int64_t rel = prow - key_base;
-        const int lim = rel < kBlk * nk - 1 ? (int)rel : kBlk * nk - 1;
-        const bool full = nk == kSplit / kBlk && p_wave - key_base >= kSplit - 1;
+        const int lim = rel < kSplit - 1 ? (int)rel : kSplit - 1;
+        const bool full = p_wave - key_base >= kSplit - 1;
         float mx = -__builtin_inff();
         if (full) {
 #pragma unroll
@@ -333,29 +352,38 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
                 pk[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(S[2 * kb + e / 4][e % 4], c2, -m_new));
             return pk;
         };
+        auto vstep = [&](const u32x4 *slot, int vc) {
 #pragma unroll
-        for (int vc = 0; vc < kSplit / kBlk; ++vc) {
-            if (vc < nk)
-                step([&](const u32x4 *slot) {
+            for (int kb2 = 0; kb2 < 2; ++kb2) {
+                const bf16x8 pk = weights(2 * vc + kb2);
+                lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk, lsum, 0, 0, 0);
+                // V^T fragments of columns ct + 1 .. ct + 2 in flight while ct multiplies
+                bf16x8 vf[4];
+                vf[0] = v_frag<D>(slot, vbase, 0, kb2);
+                vf[1] = v_frag<D>(slot, vbase, 1, kb2);
 #pragma unroll
-                    for (int kb2 = 0; kb2 < 2; ++kb2) {
-                        const bf16x8 pk = weights(2 * vc + kb2);
-                        lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pk, lsum, 0, 0, 0);
-                        // V^T fragments of columns ct + 1 .. ct + 2 in flight while ct multiplies
-                        bf16x8 vf[4];
-                        vf[0] = v_frag<D>(slot, vbase, 0, kb2);
-                        vf[1] = v_frag<D>(slot, vbase, 1, kb2);
-#pragma unroll
-                        for (int ct = 0; ct < D / 16; ++ct) {
-                            if (ct + 2 < D / 16) vf[(ct + 2) & 3] = v_frag<D>(slot, vbase, ct + 2, kb2);
-                            acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct & 3], pk,
-                                                                             acc[ct], 0, 0, 0);
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                    }
-                });
-        }
+                for (int ct = 0; ct < D / 16; ++ct) {
+                    if (ct + 2 < D / 16) vf[(ct + 2) & 3] = v_frag<D>(slot, vbase, ct + 2, kb2);
+                    acc[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[ct & 3], pk, acc[ct], 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+        };
+        dma(slot3, q0 + 7);
+        vstep(slot0, 0);
+        meet();
+        dma(slot0, q0 + 8);
+        vstep(slot1, 1);
+        meet();
+        dma(slot1, q0 + 9);
+        vstep(slot2, 2);
+        meet();
+        dma(slot2, q0 + 10);
+        vstep(slot3, 3);
+        meet();
     }
+    // drain the copies still in flight (they target the scratch kilobyte) before the end
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     if (trow < T) {
         const float inv = 1.0f / lsum[0];
