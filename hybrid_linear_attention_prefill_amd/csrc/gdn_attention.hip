@@ -20,14 +20,13 @@
 // the softmax update, then O^T += V^T P^T.  Both products put a query row in lane % 16, so the
 // row statistics and the rescaling stay inside a lane.
 //
-// Staging: a split is eight block steps (its four K blocks, then its four V blocks), and block
-// e of a split lives in LDS slot e mod 4, four separate arrays, so every step reads a slot
-// known at compile time.  Each step first issues the copy of the block three steps ahead into
-// the slot the previous step read, straight from global memory into LDS (buffer loads with the
-// LDS bit: no registers, no LDS write instructions), then runs its products, then waits until
-// this wave's copies of the next step's block have landed (the two later blocks' copies may
-// still be in flight) and meets the other waves at a barrier.  The compiler tells the four
-// slots apart, so the products' LDS reads never wait for copies bound for other slots.
+// Staging: a split is eight 64-key blocks (its four K blocks, then its four V blocks), and
+// block e of a split lives in LDS slot e mod 4, four separate arrays, so every read names a
+// slot known at compile time.  The blocks go in pairs: while a pair is multiplied, the next
+// pair is copied into the two other slots straight from global memory (buffer loads with the
+// LDS bit: no registers, no LDS write instructions); then each wave waits for its own copies
+// and the workgroup meets at a barrier, four times a split.  The compiler tells the four slots
+// apart, so the products' LDS reads never wait for the copies bound for the other two.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -126,8 +125,8 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t *p, f32x4 v)
 typedef __attribute__((address_space(3))) void lds_void;
 
 // A block's kSlotChunks<D> 16-byte chunks are filled by kNGI copy instructions of 64 lanes
-// (lane i of instruction gi fills chunk 64 gi + i); wave w issues instructions w, w + 8, ...:
-// kJ of them, or kJ - 1 in waves past kNGI mod 8.
+// (lane i of instruction gi fills chunk 64 gi + i); wave w issues instructions w, w + 8, ...
+// below kNGI: kJ of them, or kJ - 1 in waves past kNGI mod 8.
 template <int D>
 constexpr int kNGI = kSlotChunks<D> / 64;
 template <int D>
@@ -167,7 +166,6 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
 {
     __shared__ u32x4 slot0[kSlotChunks<D>], slot1[kSlotChunks<D>], slot2[kSlotChunks<D>],
         slot3[kSlotChunks<D>];
-    __shared__ u32x4 scratch_lds[64];  // where the copies of blocks past the last split go
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, g = lane >> 4;
     const int RW = kWaves / HW;  // 16-row tiles per workgroup
@@ -226,49 +224,33 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
     float m = -__builtin_inff();
     const int64_t p_wave = pos0 + tw;  // the wave's first (smallest) row position
 
-    // Block q = 8 j + e: e < 4 the K block e of split j, else its V block e - 4; it lives in
-    // slot q mod 4.  Blocks of splits past the last go to the scratch kilobyte (zeros), so that
-    // every wave issues the same copies at every step.
+    // Block q = 8 j + e: e < 4 the K block e of split j, else its V block e - 4, into slot
+    // q mod 4 (keys past the cache end read as zero); nothing past the last split.
     auto dma = [&](u32x4 *slot, int q) {
         const int j = q >> 3, e = q & 7;
+        if (j >= ns) return;
         const bool isv = e >= 4;
         const int64_t key0 = (int64_t)kSplit * j + kBlk * (e & 3);
-        const bool real = j < ns;
-        const int64_t nk = real && key0 < L ? (L - key0 < kBlk ? L - key0 : kBlk) : 0;
+        const int64_t nk = key0 < L ? (L - key0 < kBlk ? L - key0 : kBlk) : 0;
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)((isv ? vp : kp) + (real ? key0 : 0) * Hkv * D), 0, (int)(nk * Hkv * D * 2),
-            kRsrcWord3);
+            (void *)((isv ? vp : kp) + key0 * Hkv * D), 0, (int)(nk * Hkv * D * 2), kRsrcWord3);
 #pragma unroll
         for (int i = 0; i < kJ<D>; ++i) {
             const int gi = wave + kWaves * i;
-            // wave-uniform: the last round only in the waves below kNGI mod 8
-            if (i + 1 < kJ<D> || kNGI<D> % kWaves == 0 || gi < kNGI<D>) {
-                u32x4 *dst = real ? slot + 64 * gi : scratch_lds;
-                copy_to_lds(r, dst, isv ? offv[i] : offk[i]);
-            }
+            if (gi < kNGI<D>) copy_to_lds(r, slot + 64 * gi, isv ? offv[i] : offk[i]);
         }
     };
-    // this wave's copies of the next step's block have landed (those of the two blocks after it
-    // may still be in flight; the counter drops in issue order), then the workgroup meets
+    // this wave's copies have landed; then the workgroup meets (no fence: the copies are the
+    // only memory traffic of the loop, and every LDS read of a pair is consumed before it)
     auto meet = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-        // this wave's copies per block: kJ, or kJ - 1 for waves past NGI mod 8
-        const bool full_round =
-            kNGI<D> % kWaves == 0 || __builtin_amdgcn_readfirstlane(wave) < kNGI<D> % kWaves;
-        if constexpr (kJ<D> == 5) {
-            if (full_round) __builtin_amdgcn_s_waitcnt(0x0F7A);  // vmcnt(10)
-            else __builtin_amdgcn_s_waitcnt(0x0F78);             // vmcnt(8)
-        } else {
-            if (full_round) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
-            else __builtin_amdgcn_s_waitcnt(0x0F74);             // vmcnt(4)
-        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
 
     dma(slot0, 0);
     dma(slot1, 1);
-    dma(slot2, 2);
     meet();
 
     for (int j = 0; j < ns; ++j) {
@@ -293,16 +275,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
             }
         };
         const int q0 = 8 * j;
+        dma(slot2, q0 + 2);
         dma(slot3, q0 + 3);
         kstep(slot0, 0);
-        meet();
-        dma(slot0, q0 + 4);
         kstep(slot1, 1);
         meet();
+        dma(slot0, q0 + 4);
         dma(slot1, q0 + 5);
         kstep(slot2, 2);
-        meet();
-        dma(slot2, q0 + 6);
         kstep(slot3, 3);
         meet();
 
@@ -369,21 +349,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a, int Hq, int 
                 }
             }
         };
+        dma(slot2, q0 + 6);
         dma(slot3, q0 + 7);
         vstep(slot0, 0);
-        meet();
-        dma(slot0, q0 + 8);
         vstep(slot1, 1);
         meet();
+        dma(slot0, q0 + 8);
         dma(slot1, q0 + 9);
         vstep(slot2, 2);
-        meet();
-        dma(slot2, q0 + 10);
         vstep(slot3, 3);
         meet();
     }
-    // drain the copies still in flight (they target the scratch kilobyte) before the end
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     if (trow < T) {
         const float inv = 1.0f / lsum[0];
